@@ -1,0 +1,224 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the bench's CPU-baseline leg may import this
+package.  It is built from oracle.c with gcc (no fast-math, no FP contraction)
+and shares no code with the GPU library.  Each wrapper below names the C
+function it calls; the C file cites the passages each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_c_i64 = ctypes.c_longlong
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_ip = ctypes.POINTER(ctypes.c_longlong)
+_up = ctypes.POINTER(ctypes.c_ulonglong)
+
+_libs: dict = {}
+_active = None  # path of the library the module-level functions use
+
+
+def compile_library(src: str, out: str) -> str:
+    """gcc build of an oracle source file into a shared library."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared",
+           "-ffp-contract=off", "-fno-fast-math", "-pthread", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        compile_library(_SRC, _LIB)
+    return _LIB
+
+
+class use_library:
+    """Context manager: route the module functions to another build of the
+    oracle source (used by the planted-mistake tests)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _active
+        self.prev, _active = _active, self.path
+        return self
+
+    def __exit__(self, *exc):
+        global _active
+        _active = self.prev
+        return False
+
+
+def _load():
+    path = _active or _LIB
+    if path in _libs:
+        return _libs[path]
+    if path == _LIB and (not os.path.exists(_LIB)
+                         or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+        build(force=True)
+    lib = ctypes.CDLL(path)
+    lib.orc_attention.argtypes = [_fp, _fp, _fp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                  ctypes.c_int, ctypes.c_double, _ip, _c_i64, _dp, _dp,
+                                  ctypes.c_int]
+    lib.orc_attention.restype = ctypes.c_int
+    lib.orc_attention_probs.argtypes = [_fp, _fp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_i64, ctypes.c_int, ctypes.c_double, _c_i64, _c_i64,
+                                        _c_i64, _dp]
+    lib.orc_attention_probs.restype = ctypes.c_int
+    lib.orc_pcast.argtypes = [_fp, _fp, _fp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                              ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                              ctypes.c_int, _c_i64, _ip, _c_i64, _dp, _dp, _up, ctypes.c_int]
+    lib.orc_pcast.restype = ctypes.c_int
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint]
+    lib.orc_e4m3_decode.restype = ctypes.c_float
+    for name in ("orc_Phi", "orc_delta_c", "orc_dp"):
+        getattr(lib, name).restype = ctypes.c_double
+    lib.orc_Phi.argtypes = [ctypes.c_double]
+    lib.orc_delta_c.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.orc_dp.argtypes = [ctypes.c_double]
+    lib.orc_F.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    lib.orc_F.restype = ctypes.c_double
+    lib.orc_expected_max_gauss.argtypes = [ctypes.c_int]
+    lib.orc_expected_max_gauss.restype = ctypes.c_double
+    _libs[path] = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _rows_arg(rows, B, H, Nq):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if r.ndim == 1:
+        r = np.broadcast_to(r, (B * H, r.shape[0])).copy()
+    r = r.reshape(B * H, -1)
+    return r, r.shape[1]
+
+
+def attention(q, k, v, causal: bool, scale: float, rows=None, nthreads: int | None = None):
+    """orc_attention: exact O [B,H,R,d] (float64) and LSE [B,H,R].
+
+    q: [B,H,Nq,d], k/v: [B,Hkv,Nk,d], given as float32 arrays holding the exact
+    values handed to the GPU (bf16/fp16 widen exactly).  rows: None (all Nq
+    rows), a 1-D row list used for every (b,h), or a [B*H, R] array.
+    """
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    r, R = _rows_arg(rows, B, H, Nq)
+    if r is None:
+        R = Nq
+    o = np.zeros((B, H, R, d), dtype=np.float64)
+    lse = np.zeros((B, H, R), dtype=np.float64)
+    rc = lib.orc_attention(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, H, Hkv, Nq, Nk, d,
+                           int(bool(causal)), float(scale),
+                           None if r is None else _ptr(r, _ip), R, _ptr(o, _dp),
+                           _ptr(lse, _dp), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"orc_attention rejected its arguments (rc={rc})")
+    return o, lse
+
+
+def attention_probs(q, k, causal: bool, scale: float, b: int, h: int, i: int) -> np.ndarray:
+    """orc_attention_probs: the probability row of query (b,h,i), length Nk."""
+    lib = _load()
+    q, k = _f32(q), _f32(k)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    p = np.zeros(Nk, dtype=np.float64)
+    rc = lib.orc_attention_probs(_ptr(q, _fp), _ptr(k, _fp), B, H, Hkv, Nq, Nk, d,
+                                 int(bool(causal)), float(scale), b, h, i, _ptr(p, _dp))
+    if rc != 0:
+        raise ValueError("orc_attention_probs rejected its arguments")
+    return p
+
+
+def pcast_emulate(q, k, v, causal: bool, scale: float, kv_tile: int, p_scale: float,
+                  reverse: bool, n_sink: int = 0, rows=None, nthreads: int | None = None):
+    """orc_pcast: E4M3 P-cast emulation.
+
+    Returns (O, LSE, counts) with counts = [casts, zeros] over keys >= n_sink
+    followed by [casts, zeros] over keys outside the KV tiles holding a sink.
+    """
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    r, R = _rows_arg(rows, B, H, Nq)
+    if r is None:
+        R = Nq
+    o = np.zeros((B, H, R, d), dtype=np.float64)
+    lse = np.zeros((B, H, R), dtype=np.float64)
+    counts = np.zeros(4, dtype=np.uint64)
+    rc = lib.orc_pcast(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, H, Hkv, Nq, Nk, d,
+                       int(bool(causal)), float(np.float32(scale)), int(kv_tile),
+                       float(np.float32(p_scale)), int(bool(reverse)), int(n_sink),
+                       None if r is None else _ptr(r, _ip), R, _ptr(o, _dp), _ptr(lse, _dp),
+                       _ptr(counts, _up), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"orc_pcast rejected its arguments (rc={rc})")
+    return o, lse, [int(c) for c in counts]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    lib = _load()
+    xs = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.orc_e4m3_encode(float(t)) for t in xs], dtype=np.uint8).reshape(
+        np.shape(x))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    cs = np.asarray(codes, dtype=np.int64).ravel()
+    return np.array([lib.orc_e4m3_decode(int(c)) for c in cs], dtype=np.float32).reshape(
+        np.shape(codes))
+
+
+def Phi(x: float) -> float:
+    return _load().orc_Phi(float(x))
+
+
+def F_closed_form(delta: float, S: float, delta_k: float) -> float:
+    return _load().orc_F(float(delta), float(S), float(delta_k))
+
+
+def delta_c(S: float, delta_k: float) -> float:
+    return _load().orc_delta_c(float(S), float(delta_k))
+
+
+def expected_max_gauss(k: int) -> float:
+    return _load().orc_expected_max_gauss(int(k))
+
+
+def dp(S: float) -> float:
+    return _load().orc_dp(float(S))

@@ -1,0 +1,390 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg load this library.  It shares no code, header, table or
+ * helper with the GPU library; both sides only consume the same seeded input
+ * buffers.  Build: gcc -O2 -ffp-contract=off (no -ffast-math), so every
+ * floating-point step below is one plain IEEE double operation.
+ *
+ * Pages cited (title, then section):
+ *  [MM] marketmaker.cc, "Atencion flash y la pregunta sobre la longitud de la
+ *       secuencia" (Spanish blog post on flash attention for trading models)
+ *  [SA] systems-analysis.info, "FlashAttention (IT)" (encyclopedia entry)
+ *  [PC] gist.science, "Resumen Tecnico: Precision de P-Cast en la Atencion FP8"
+ *  [FV] gist.science, "FlashAttention for Scalable Vector Architectures"
+ *
+ * Parity status of each function (what pins it is in tests/test_oracle_*.py):
+ *  orc_attention ....... pinned (brute force at 50 digits, torch fp64 SDPA,
+ *                         closed forms, invariants, online recurrence)
+ *  orc_attention_probs . pinned (rows sum to 1, same pins as above)
+ *  orc_pcast ........... pinned (identity case vs orc_attention, underflow
+ *                         fraction vs the closed form F, reverse-order zero
+ *                         count, brute-force tiny case)
+ *  orc_e4m3_* .......... pinned (OCP constants printed on [PC], torch float8)
+ *  orc_F, orc_delta_c .. pinned (printed constants and thresholds of [PC],
+ *                         Monte Carlo of the model)
+ *  orc_expected_max_gauss pinned (k=1 -> 0, k=2 -> 1/sqrt(pi), Monte Carlo)
+ *  orc_dp .............. pinned (the two facts printed on [PC] "Optimizacion 2")
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef long long i64;
+typedef unsigned long long u64;
+
+/* ------------------------------------------------------------------------ */
+/* Exact attention by its definition.                                       */
+/*                                                                          */
+/* [MM] "Por que la atencion esta ligada a la memoria" and [SA]             */
+/* "Problematica dell'attention standard" define                            */
+/*     O = softmax(Q K^T * scale) V,   scale = 1/sqrt(d_k),                 */
+/* with the score matrix S = Q K^T * scale formed in full.  Here each score */
+/* row is formed completely before its softmax (two passes over the row:    */
+/* max, then exponentials and their sum), which is the plain definition.    */
+/*                                                                          */
+/* Readings where the pages are silent:                                     */
+/*  - causal masking ([MM] "El enmascaramiento causal..."): key j is        */
+/*    visible to query i iff j <= i + (Nk - Nq) (bottom-right alignment;    */
+/*    equals the usual j <= i when Nq == Nk);                               */
+/*  - GQA ([FV] "Metodologia": shared KV heads): query head h reads KV head */
+/*    h / (H / Hkv);                                                        */
+/*  - the per-row statistics (m, l) ([MM] "Pase hacia atras") are reported  */
+/*    as LSE = m + ln(l) in natural log; a row with no visible key has      */
+/*    O = 0 and LSE = -inf.                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *q, *k, *v;
+    i64 B, H, Hkv, Nq, Nk, d;
+    int causal;
+    double scale;
+    const i64 *rows;   /* [B*H][nrows] or NULL (all rows) */
+    i64 nrows;
+    double *o, *lse;
+    /* p-cast emulation */
+    int pcast;
+    int kv_tile;
+    float p_scale;
+    float scale_f;
+    int reverse;
+    i64 n_sink;
+    /* work distribution */
+    i64 n_items;
+    i64 next;          /* atomic */
+    u64 cnt[4];        /* atomic */
+} job_t;
+
+static i64 visible_count(const job_t *J, i64 i)
+{
+    if (!J->causal) return J->Nk;
+    i64 lim = i + (J->Nk - J->Nq) + 1;
+    if (lim < 0) lim = 0;
+    if (lim > J->Nk) lim = J->Nk;
+    return lim;
+}
+
+static double dot(const float *a, const float *b, i64 d)
+{
+    double acc = 0.0;
+    for (i64 c = 0; c < d; ++c) acc += (double)a[c] * (double)b[c];
+    return acc;
+}
+
+/* One row of the definition: fills s[0..lim) with the scores, then p. */
+static void exact_row(const job_t *J, i64 b, i64 h, i64 i, double *s, double *o_row,
+                      double *lse_out)
+{
+    const i64 d = J->d, g = J->H / J->Hkv, hk = h / g;
+    const float *qi = J->q + ((b * J->H + h) * J->Nq + i) * d;
+    const float *kb = J->k + (b * J->Hkv + hk) * J->Nk * d;
+    const float *vb = J->v + (b * J->Hkv + hk) * J->Nk * d;
+    const i64 lim = visible_count(J, i);
+    for (i64 c = 0; c < d; ++c) o_row[c] = 0.0;
+    if (lim == 0) { *lse_out = -INFINITY; return; }
+    double m = -INFINITY;
+    for (i64 j = 0; j < lim; ++j) {
+        s[j] = J->scale * dot(qi, kb + j * d, d);
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (i64 j = 0; j < lim; ++j) { s[j] = exp(s[j] - m); l += s[j]; }
+    for (i64 j = 0; j < lim; ++j) {
+        const double p = s[j] / l;
+        const float *vj = vb + j * d;
+        for (i64 c = 0; c < d; ++c) o_row[c] += p * (double)vj[c];
+    }
+    *lse_out = m + log(l);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP 8-bit floating point, "E4M3FN" variant): 1 sign bit, 4        */
+/* exponent bits with bias 7, 3 mantissa bits, no infinities, the all-ones  */
+/* magnitude 0x7F is NaN.  Largest finite 448, smallest normal 2^-6,        */
+/* subnormals m * 2^-9.  [PC] "Planteamiento del Problema" names the format */
+/* (3-bit mantissa); [PC] "Marco Teorico" gives the round-to-zero threshold */
+/* 2^-10 and "Optimizacion 2" the bound S <= 448 and 2^-6.                  */
+/* Encoding rounds to nearest, ties to even; magnitudes at or above 464     */
+/* (the midpoint above 448) saturate to 448.                                */
+/* ------------------------------------------------------------------------ */
+
+float orc_e4m3_decode(unsigned code)
+{
+    code &= 0xFF;
+    const int sgn = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double a;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) a = ldexp((double)m, -9);
+    else a = ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(sgn ? -a : a);
+}
+
+unsigned orc_e4m3_encode(float x)
+{
+    if (isnan(x)) return 0x7F;
+    const unsigned sgn = signbit(x) ? 0x80u : 0u;
+    const double a = fabs((double)x);
+    if (a >= 464.0) return sgn | 0x7Eu;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid m * 2^-9; the product is exact, nearbyint is RNE */
+        const double qv = nearbyint(a * 512.0);
+        return sgn | (unsigned)qv;           /* qv == 8 is the code of 2^-6 */
+    }
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                          /* a in [2^E, 2^(E+1)) */
+    double qv = nearbyint(ldexp(a, 3 - E));  /* in [8, 16] */
+    if (qv == 16.0) { qv = 8.0; E += 1; }
+    return sgn | ((unsigned)(E + 7) << 3) | (unsigned)(qv - 8.0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* P-cast emulation.  [PC] "Planteamiento del Problema": the softmax        */
+/* probabilities P are cast to E4M3 before the P*V product, after being     */
+/* multiplied by a static scale S that is divided back out at the end; the  */
+/* KV blocks of the online softmax run forward (0 -> N) or in reverse       */
+/* (N -> 0) ("Optimizacion 1").  P is taken relative to the RUNNING maximum */
+/* m, which is what lets early sink logits push later non-sink P under the  */
+/* E4M3 range (the P-collapse described there).  [PC] "Contribuciones      */
+/* Clave" item 4: Q, K, V stay in FP32, so the cast is the only reduced-    */
+/* precision step.                                                          */
+/*                                                                          */
+/* Steps per query row (online recurrence of [MM] "La recurrencia de        */
+/* softmax en linea": running max, running sum, accumulator rescaled by     */
+/* e^(m_old - m_new)):                                                      */
+/*   for each KV tile t of width kv_tile meeting the visible keys, in order:*/
+/*     s_j  = fp32(scale * q.k_j)                   (fp32 logit)            */
+/*     m'   = max(m, max_j s_j)                     (fp32)                  */
+/*     a    = exp(m - m')                                                   */
+/*     p_j  = fp32(exp(s_j - m'))                   (fp32, kernel precision)*/
+/*     l    = a*l + sum_j p_j                       (sum of the uncast p)   */
+/*     pt_j = E4M3(fp32(S * p_j))                   (the cast decision, fp32)*/
+/*     acc  = a*acc + sum_j pt_j * v_j;  m = m'                             */
+/*   O = acc / (S * l),  LSE = m + ln l                                     */
+/* Counters: casts, and zeros (pt == 0 while p > 0), over two key sets:    */
+/*   [0],[1] keys j >= n_sink (every non-sink key);                         */
+/*   [2],[3] keys outside the KV tiles that hold a sink key (j >= the first */
+/*           tile boundary at or after n_sink).  Non-sink keys that share a */
+/*           tile with a sink are cast after the running max has absorbed   */
+/*           the sink logits in either order; [PC] "Optimizacion 1" claims  */
+/*           zero underflow for the values cast BEFORE the sink block.      */
+/* ------------------------------------------------------------------------ */
+
+static void pcast_row(job_t *J, i64 b, i64 h, i64 i, double *o_row, double *lse_out,
+                      u64 *cnt)
+{
+    const i64 d = J->d, g = J->H / J->Hkv, hk = h / g, Bc = J->kv_tile;
+    const float *qi = J->q + ((b * J->H + h) * J->Nq + i) * d;
+    const float *kb = J->k + (b * J->Hkv + hk) * J->Nk * d;
+    const float *vb = J->v + (b * J->Hkv + hk) * J->Nk * d;
+    const i64 lim = visible_count(J, i);
+    for (i64 c = 0; c < d; ++c) o_row[c] = 0.0;
+    if (lim == 0) { *lse_out = -INFINITY; return; }
+    const i64 ntiles = (lim + Bc - 1) / Bc;
+    const i64 sink_end = ((J->n_sink + Bc - 1) / Bc) * Bc;
+    float s[1024];
+    float m = -INFINITY;
+    double l = 0.0;
+    for (i64 tt = 0; tt < ntiles; ++tt) {
+        const i64 t = J->reverse ? (ntiles - 1 - tt) : tt;
+        const i64 j0 = t * Bc;
+        const i64 j1 = (j0 + Bc < lim) ? j0 + Bc : lim;
+        float mn = m;
+        for (i64 j = j0; j < j1; ++j) {
+            s[j - j0] = (float)((double)J->scale_f * dot(qi, kb + j * d, d));
+            if (s[j - j0] > mn) mn = s[j - j0];
+        }
+        const double a = (m == -INFINITY) ? 0.0 : exp((double)m - (double)mn);
+        l *= a;
+        for (i64 c = 0; c < d; ++c) o_row[c] *= a;
+        for (i64 j = j0; j < j1; ++j) {
+            const float p = (float)exp((double)s[j - j0] - (double)mn);
+            l += (double)p;
+            const float x = p * J->p_scale;
+            const float pt = orc_e4m3_decode(orc_e4m3_encode(x));
+            const int flushed = (pt == 0.0f && p > 0.0f);
+            if (j >= J->n_sink) { cnt[0] += 1; cnt[1] += flushed; }
+            if (j >= sink_end) { cnt[2] += 1; cnt[3] += flushed; }
+            const float *vj = vb + j * d;
+            for (i64 c = 0; c < d; ++c) o_row[c] += (double)pt * (double)vj[c];
+        }
+        m = mn;
+    }
+    const double den = (double)J->p_scale * l;
+    for (i64 c = 0; c < d; ++c) o_row[c] /= den;
+    *lse_out = (double)m + log(l);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Threading: items are (b, h, row) in row-major order, handed out in small */
+/* chunks from an atomic counter.  Each item writes only its own outputs.   */
+/* ------------------------------------------------------------------------ */
+
+static void *worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    const i64 per_bh = J->rows ? J->nrows : J->Nq;
+    double *s = J->pcast ? NULL : (double *)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
+    u64 cnt[4] = {0, 0, 0, 0};
+    for (;;) {
+        const i64 start = __atomic_fetch_add(&J->next, 8, __ATOMIC_RELAXED);
+        if (start >= J->n_items) break;
+        const i64 end = start + 8 < J->n_items ? start + 8 : J->n_items;
+        for (i64 it = start; it < end; ++it) {
+            const i64 bh = it / per_bh, r = it % per_bh;
+            const i64 b = bh / J->H, h = bh % J->H;
+            const i64 i = J->rows ? J->rows[bh * J->nrows + r] : r;
+            double *o_row = J->o + it * J->d;
+            if (J->pcast) pcast_row(J, b, h, i, o_row, J->lse + it, cnt);
+            else exact_row(J, b, h, i, s, o_row, J->lse + it);
+        }
+    }
+    for (int c = 0; c < 4; ++c) __atomic_fetch_add(&J->cnt[c], cnt[c], __ATOMIC_RELAXED);
+    free(s);
+    return NULL;
+}
+
+static int run(job_t *J, int nthreads)
+{
+    if (J->B < 0 || J->H < 1 || J->Hkv < 1 || J->H % J->Hkv || J->Nq < 0 || J->Nk < 0 || J->d < 1)
+        return -1;
+    if (J->rows) {
+        for (i64 x = 0; x < J->B * J->H * J->nrows; ++x)
+            if (J->rows[x] < 0 || J->rows[x] >= J->Nq) return -2;
+    }
+    if (J->pcast && (J->kv_tile < 1 || J->kv_tile > 1024)) return -3;
+    J->n_items = J->B * J->H * (J->rows ? J->nrows : J->Nq);
+    J->next = 0;
+    J->cnt[0] = J->cnt[1] = J->cnt[2] = J->cnt[3] = 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[started], NULL, worker, J) == 0) ++started;
+    worker(J);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* o: [B,H,R,d], lse: [B,H,R] where R = nrows (rows != NULL) or Nq. */
+int orc_attention(const float *q, const float *k, const float *v, i64 B, i64 H, i64 Hkv,
+                  i64 Nq, i64 Nk, i64 d, int causal, double scale, const i64 *rows,
+                  i64 nrows, double *o, double *lse, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.B = B; J.H = H; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
+    J.causal = causal; J.scale = scale; J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
+    return run(&J, nthreads);
+}
+
+/* The full probability row p[0..Nk) of query (b,h,i); invisible keys get 0. */
+int orc_attention_probs(const float *q, const float *k, i64 B, i64 H, i64 Hkv, i64 Nq,
+                        i64 Nk, i64 d, int causal, double scale, i64 b, i64 h, i64 i,
+                        double *p)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = k; J.B = B; J.H = H; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
+    J.causal = causal; J.scale = scale;
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Nq || H % Hkv) return -1;
+    const i64 g = H / Hkv, hk = h / g;
+    const float *qi = q + ((b * H + h) * Nq + i) * d;
+    const float *kb = k + (b * Hkv + hk) * Nk * d;
+    const i64 lim = visible_count(&J, i);
+    for (i64 j = 0; j < Nk; ++j) p[j] = 0.0;
+    if (lim == 0) return 0;
+    double m = -INFINITY, l = 0.0;
+    for (i64 j = 0; j < lim; ++j) {
+        p[j] = scale * dot(qi, kb + j * d, d);
+        if (p[j] > m) m = p[j];
+    }
+    for (i64 j = 0; j < lim; ++j) { p[j] = exp(p[j] - m); l += p[j]; }
+    for (i64 j = 0; j < lim; ++j) p[j] /= l;
+    return 0;
+}
+
+int orc_pcast(const float *q, const float *k, const float *v, i64 B, i64 H, i64 Hkv, i64 Nq,
+              i64 Nk, i64 d, int causal, float scale, int kv_tile, float p_scale, int reverse,
+              i64 n_sink, const i64 *rows, i64 nrows, double *o, double *lse,
+              u64 *counts /* [4], see pcast_row */, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.B = B; J.H = H; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
+    J.causal = causal; J.scale = (double)scale; J.scale_f = scale; J.rows = rows;
+    J.nrows = nrows; J.o = o; J.lse = lse;
+    J.pcast = 1; J.kv_tile = kv_tile; J.p_scale = p_scale; J.reverse = reverse;
+    J.n_sink = n_sink;
+    const int rc = run(&J, nthreads);
+    if (counts) for (int c = 0; c < 4; ++c) counts[c] = J.cnt[c];
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Closed forms of [PC] "Marco Teorico" and "Optimizacion 2".               */
+/* ------------------------------------------------------------------------ */
+
+/* Standard normal CDF. */
+double orc_Phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/* Fraction of non-sink P values flushed to zero under forward KV order:
+ * F(Delta, S) = Phi(Delta + delta_k - 10 ln 2 - ln S).  The page writes the
+ * constant as 6.93 and identifies it with 10 ln 2, the log of the E4M3
+ * round-to-zero threshold 2^-10. */
+double orc_F(double delta, double S, double delta_k)
+{
+    return orc_Phi(delta + delta_k - 10.0 * log(2.0) - log(S));
+}
+
+/* Collapse threshold Delta_c = 10 ln 2 + ln S - delta_k (where F = 1/2). */
+double orc_delta_c(double S, double delta_k) { return 10.0 * log(2.0) + log(S) - delta_k; }
+
+/* delta_k = E[max of k iid N(0,1)] = int x * k phi(x) Phi(x)^(k-1) dx,
+ * composite Simpson rule on [-12, 12] (the integrand is below 1e-30 outside). */
+double orc_expected_max_gauss(int k)
+{
+    const int n = 48000;
+    const double a = -12.0, b = 12.0, hstep = (b - a) / n;
+    double acc = 0.0;
+    for (int i = 0; i <= n; ++i) {
+        const double x = a + i * hstep;
+        const double f = x * k * exp(-0.5 * x * x) / sqrt(2.0 * M_PI) * pow(orc_Phi(x), k - 1);
+        const double w = (i == 0 || i == n) ? 1.0 : ((i & 1) ? 4.0 : 2.0);
+        acc += w * f;
+    }
+    return acc * hstep / 3.0;
+}
+
+/* d_p(S): the E4M3 quantisation step just below S, divided by S.  For S in
+ * (2^(k-1), 2^k] the values just below S lie in the binade [2^(k-1), 2^k)
+ * whose spacing is 2^(k-1-3). */
+double orc_dp(double S)
+{
+    const double k = ceil(log2(S));
+    return ldexp(1.0, (int)k - 4) / S;
+}
