@@ -1,0 +1,203 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one causal bf16 prefill (fa_fwd) over the full-trading-day workload
+(B=1, H=12, N=23,400, d=64, AR(1)+noise inputs, seeded).  The line printed
+also carries the split-KV GQA decode (fa_decode) on the TinyLlama-shaped
+cache (B=16, 32/4 heads, Nk=8192, d=64, bf16), each with its roofline, and
+the fp64 CPU oracle timed on a bounded sample of the prefill rows.
+
+Timing: HIP events on the stream the kernels are launched on (torch's current
+stream), around exactly K calls after W warm-up calls, bracketed by device
+synchronisation.  A spin kernel is queued ahead of the timed region so every
+call is already enqueued when the GPU reaches the first one; host launch
+overhead therefore does not enter the measured time.  Decode rotates over
+four KV caches (4 x 134 MB, more than the 256 MB last-level cache) so each
+call reads its cache from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd attn TFLOP/s & % MFMA peak (N=23.4k causal); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # HBM3E
+PREFILL_KERNEL = "exact_io_aware_08_amd/csrc/fa_fwd_mfma.hip"
+DECODE_KERNEL = "exact_io_aware_08_amd/csrc/fa_decode.hip"
+
+
+def _sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(summary, kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None if
+    the summary is missing or the kernel source changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != _sha(kernel_src):
+        return None
+    return float(m_b.group(1))
+
+
+def _timed(fn, steps, warmup, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e7))       # queue ahead: the GPU is busy while we enqueue
+    start.record(st)
+    for i in range(steps):
+        fn(i)
+    end.record(st)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps   # ms per call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head (CPU leg)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_08_amd as fa
+    import fagen
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+
+    # ---------------- prefill: the step ----------------
+    c3 = fagen.CONFIGS[3]
+    B, H, N, d = c3["B"], c3["H"], c3["Nq"], c3["d"]
+    q3n, k3n, v3n = fagen.make_inputs(c3, 0)
+    q3, k3, v3 = to_dev(q3n, "bf16"), to_dev(k3n, "bf16"), to_dev(v3n, "bf16")
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flops = 2.0 * d * B * H * N * (N + 1)        # 4d per visible (query, key) pair
+    if args.only in ("all", "prefill"):
+        ms = _timed(lambda i: fa.fwd(q3, k3, v3, causal=True, scale=c3["scale"], out=o3, lse=l3),
+                    args.steps, args.warmup, torch)
+        tflops = flops / (ms * 1e-3) / 1e12
+        traffic = _traffic("fa_fwd_trading_day_bf16_pmc.md", PREFILL_KERNEL)
+        out.update({
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+            "config": {"workload": "trading_day_prefill_bf16", "B": B, "H": H, "Nq": N, "Nk": N,
+                       "d": d, "causal": True, "inputs": "AR(1) phi=0.9 + N(0,0.1) noise, seed 0",
+                       "algorithmic_flop": flops},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic},
+        })
+
+    # ---------------- decode ----------------
+    if args.only in ("all", "decode"):
+        c4 = fagen.CONFIGS[4]
+        B4, H4, Hkv4, Nk4, d4 = c4["B"], c4["H"], c4["Hkv"], c4["Nk"], c4["d"]
+        q4n, k4n, v4n = fagen.make_inputs(c4, 0)
+        q4 = to_dev(q4n, "bf16")
+        caches = [(to_dev(k4n, "bf16"), to_dev(v4n, "bf16"))]
+        for r in range(1, 4):   # independent copies so consecutive calls miss the cache
+            caches.append((caches[0][0].clone(), caches[0][1].clone()))
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty((B4, H4, 1), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.decode_workspace_bytes(B4, H4, Hkv4, Nk4, d4), dtype=torch.uint8,
+                         device=dev)
+        dbytes = 2 * B4 * Hkv4 * Nk4 * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4
+        us = 1e3 * _timed(lambda i: fa.decode(q4, caches[i % 4][0], caches[i % 4][1],
+                                              scale=c4["scale"], workspace=ws, out=o4, lse=l4),
+                          args.decode_steps, 8, torch)
+        gbs = dbytes / (us * 1e-6) / 1e9
+        dec = {"workload": "gqa_decode_bf16", "B": B4, "H": H4, "Hkv": Hkv4, "Nk": Nk4, "d": d4,
+               "splits": fa.decode_splits(B4, H4, Hkv4, Nk4), "value": round(gbs, 1),
+               "unit": "GB/s", "us_per_call": round(us, 2), "algorithmic_bytes": dbytes,
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": _traffic("fa_decode_gqa_bf16_pmc.md", DECODE_KERNEL),
+                            "timed": "split + merge kernels per call"}}
+        if args.only == "decode":
+            out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
+                        "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})
+        out["decode"] = dec
+
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+
+    # ---------------- parity on sampled rows + CPU baseline ----------------
+    if args.only in ("all", "prefill") and not args.no_cpu_baseline:
+        import oracle
+
+        rows = np.stack([fagen.sample_rows(0, h, N, args.cpu_rows) for h in range(H)])
+        wq, wk, wv = (fagen.storage_to_f32(x, "bf16") for x in (q3n, k3n, v3n))
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attention(wq, wk, wv, True, c3["scale"], rows=rows, nthreads=threads)
+        cpu_s = time.perf_counter() - t0
+        pairs = float((rows + 1).sum())
+        cpu_tflops = 4.0 * d * pairs / cpu_s / 1e12
+        og = o3.float().cpu().numpy()[0][np.arange(H)[:, None], rows]
+        lg = l3.cpu().numpy()[0][np.arange(H)[:, None], rows]
+        err = np.abs(og - o_ref[0])
+        out["parity"] = {"rows_per_head": int(rows.shape[1]), "max_abs": float(err.max()),
+                         "mean_abs": float(err.mean()),
+                         "lse_max_abs": float(np.abs(lg - l_ref[0]).max()),
+                         "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3
+                                    and np.abs(lg - l_ref[0]).max() <= 1e-3)}
+        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{rows.shape[1]} seeded rows per head x {H} heads of the "
+                                         f"N=23,400 causal prefill ({pairs:.3g} visible pairs, "
+                                         f"{cpu_s:.1f} s wall); fp64 correctness oracle, not an "
+                                         f"optimised CPU baseline"}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+"""libfa -- exact IO-aware attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of include/fa.h: it checks tensor
+placement, dtype and layout, allocates outputs with torch and passes raw
+device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the HIP kernels of libfa.so; there is no Python or CPU
+path.
+
+    o, lse = fwd(q, k, v, causal=True)                       # prefill
+    o, lse, counts = fwd_pcast(q, k, v, causal=True, p_scale=256.0, kv_reverse=True)
+    o, lse = decode(q, k_cache, v_cache)                     # split-KV GQA decode
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import FA_BF16, FA_F16, FA_F32, FaError, check, load
+
+__all__ = ["fwd", "fwd_pcast", "decode", "cast_e4m3", "kv_tile", "decode_splits",
+           "decode_workspace_bytes", "version", "FaError", "load"]
+
+_DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+
+def _stream_ptr(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check_tensor(name, t, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims [B, heads, seq, d], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+
+
+def _qkv_shapes(q, k, v):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(n, t, 4)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and k disagree on batch or head_dim")
+    return B, H, Hkv, Nq, Nk, d
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        return_lse: bool = True, stream=None):
+    """Forward attention.  q: [B,H,Nq,d]; k, v: [B,Hkv,Nk,d]; returns (o, lse)."""
+    B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None, B, H, Hkv, Nq, Nk, d,
+                       int(bool(causal)), float(scale), _DT[q.dtype], _stream_ptr(stream))
+    check(st, "fa_fwd")
+    return o, lse
+
+
+def fwd_pcast(q, k, v, causal: bool = True, scale: float | None = None, p_scale: float = 256.0,
+              kv_reverse: bool = True, n_sink: int = 0, counts=None, out=None, lse=None,
+              stream=None):
+    """E4M3 P-cast forward (fp32 q, k, v).  Returns (o, lse, counts) where
+    counts (int64 device tensor of 4) holds [non-sink casts, non-sink flushes,
+    casts outside the sink tiles, flushes outside the sink tiles]."""
+    B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if counts is None:
+        counts = torch.zeros(4, dtype=torch.int64, device=q.device)
+    st = load().fa_fwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
+                             float(scale), _DT[q.dtype], float(p_scale), int(bool(kv_reverse)),
+                             int(n_sink), counts.data_ptr(), _stream_ptr(stream))
+    check(st, "fa_fwd_pcast")
+    return o, lse, counts
+
+
+def decode_splits(B: int, H: int, Hkv: int, Nk: int, num_splits: int = 0) -> int:
+    return load().fa_decode_splits(B, H, Hkv, Nk, num_splits)
+
+
+def decode_workspace_bytes(B: int, H: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits))
+
+
+def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
+           workspace=None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Split-KV decode.  q: [B,H,1,d]; k_cache, v_cache: [B,Hkv,Nk,d]."""
+    B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k_cache, v_cache)
+    if Nq != 1:
+        raise ValueError("decode takes one query token per (batch, head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    st = load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, B, H, Hkv, Nk, d,
+                          float(scale), _DT[q.dtype], int(num_splits), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    check(st, "fa_decode")
+    return o, lse
+
+
+def cast_e4m3(x, stream=None):
+    """Device E4M3 round trip used by the P-cast kernel: (codes uint8, values fp32)."""
+    if x.device.type != "cuda" or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 GPU tensor")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    back = torch.empty_like(x)
+    st = load().fa_cast_e4m3(x.data_ptr(), codes.data_ptr(), back.data_ptr(), x.numel(),
+                             _stream_ptr(stream))
+    check(st, "fa_cast_e4m3")
+    return codes, back
+
+
+def kv_tile(dtype: torch.dtype, d: int, pcast: bool = False) -> int:
+    return load().fa_kv_tile(_DT[dtype], d, int(bool(pcast)))
+
+
+def version() -> int:
+    return load().fa_version()

@@ -1,0 +1,231 @@
+// fa_api.cpp -- the C ABI of libfa (declared in include/fa.h): host-side
+// validation, device check, and dispatch to the gfx950 kernels.
+//
+// Every argument is checked before anything is launched; on an error the
+// call returns a status and writes nothing.  There is no fallback path: an
+// unsupported combination is an error (the risk of silent fallback is the
+// point made in marketmaker.cc, "La integracion es de ocho lineas").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+// 1 if the current device is gfx950, 0 if not, -1 if it cannot be queried.
+int current_device_ok()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            g_dev_ok[dev] = -1;
+            return;
+        }
+        g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    });
+    return g_dev_ok[dev];
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status device_status()
+{
+    const int ok = current_device_ok();
+    return ok == 1 ? FA_OK : FA_ERR_DEVICE;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+constexpr long long kMaxSlice = (1LL << 31) - 1;
+
+// Shape checks common to the forward entry points (pointers checked apart).
+fa_status check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (H % Hkv != 0) return FA_ERR_GQA;
+    if ((long long)Nq * d > kMaxSlice || (long long)Nk * d > kMaxSlice) return FA_ERR_SHAPE;
+    const long long qtiles = ((long long)Nq + fa::kFwdQTile - 1) / fa::kFwdQTile;
+    if (qtiles * B * H > kMaxSlice) return FA_ERR_SHAPE;
+    if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+    return FA_OK;
+}
+
+// Pointers of empty tensors may be NULL: q, o, lse are only needed when
+// B*Nq > 0, and k, v when B*Nk > 0.
+fa_status check_fwd_ptrs(const void *q, const void *k, const void *v, const void *o,
+                         const void *lse, int B, int Nq, int Nk)
+{
+    const bool need_q = B > 0 && Nq > 0, need_kv = B > 0 && Nk > 0;
+    if ((need_q && (!q || !o)) || (need_kv && (!k || !v))) return FA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+    if (lse && !aligned16(lse)) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+int auto_splits(int B, int H, int Hkv, int Nk)
+{
+    const int G = H / Hkv;
+    const long long base = (long long)B * Hkv * ((G + 15) / 16);
+    if (base <= 0 || Nk <= 0) return 1;
+    // about 1024 workgroups (4 per CU), no split shorter than 256 keys
+    long long s = (1024 + base - 1) / base;
+    const long long max_s = ((long long)Nk + 255) / 256;
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+    if (s > 4096) s = 4096;
+    return (int)s;
+}
+
+int decode_chunk(int Nk, int splits)
+{
+    long long ch = ((long long)Nk + splits - 1) / splits;
+    ch = ((ch + fa::kDecodeStep - 1) / fa::kDecodeStep) * fa::kDecodeStep;
+    return ch < fa::kDecodeStep ? fa::kDecodeStep : (int)ch;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
+                 void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale);
+    if (s != FA_OK) return s;
+    if ((s = check_fwd_ptrs(q, k, v, o, lse, B, Nq, Nk)) != FA_OK) return s;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (B == 0 || Nq == 0) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::FwdProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d;
+    p.causal = causal; p.scale = scale; p.dtype = (int)dtype;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == FA_F32) return hip_status(fa::launch_fwd_f32(p, st));
+    return hip_status(fa::launch_fwd_mfma(p, st));
+}
+
+fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                       int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                       fa_dtype dtype, float p_scale, int kv_reverse, int n_sink,
+                       unsigned long long *counts, void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale);
+    if (s != FA_OK) return s;
+    if ((s = check_fwd_ptrs(q, k, v, o, lse, B, Nq, Nk)) != FA_OK) return s;
+    if (counts && (reinterpret_cast<uintptr_t>(counts) & 7u)) return FA_ERR_ALIGN;
+    if (dtype != FA_F32) return FA_ERR_DTYPE;
+    if (!(std::isfinite(p_scale) && p_scale > 0.f && p_scale <= 448.f)) return FA_ERR_SCALE;
+    if ((causal != 0 && causal != 1) || (kv_reverse != 0 && kv_reverse != 1) || n_sink < 0)
+        return FA_ERR_ARG;
+    if (B == 0 || Nq == 0) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::FwdProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d;
+    p.causal = causal; p.scale = scale; p.dtype = (int)dtype;
+    p.pcast = 1; p.p_scale = p_scale; p.kv_reverse = kv_reverse; p.n_sink = n_sink;
+    p.counts = counts;
+    return hip_status(fa::launch_fwd_f32(p, static_cast<hipStream_t>(stream)));
+}
+
+int fa_kv_tile(fa_dtype dtype, int d, int pcast)
+{
+    if (d != 64 && d != 128) return -1;
+    if (dtype == FA_F32) return fa::fwd_f32_kv_tile(d);
+    if (pcast) return -1;
+    if (dtype == FA_F16 || dtype == FA_BF16) return fa::kFwdKvTile;
+    return -1;
+}
+
+int fa_decode_splits(int B, int H, int Hkv, int Nk, int num_splits)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || H % Hkv || Nk < 0 || num_splits < 0 || num_splits > 4096)
+        return -1;
+    return num_splits > 0 ? num_splits : auto_splits(B, H, Hkv, Nk);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits)
+{
+    const int s = fa_decode_splits(B, H, Hkv, Nk, num_splits);
+    if (s < 0 || (d != 64 && d != 128)) return 0;
+    const size_t rows = (size_t)B * (size_t)H * (size_t)s;
+    const size_t o_bytes = ((rows * (size_t)d * sizeof(float)) + 255) & ~(size_t)255;
+    return o_bytes + rows * sizeof(float);
+}
+
+fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, void *o, float *lse,
+                    int B, int H, int Hkv, int Nk, int d, float scale, fa_dtype dtype,
+                    int num_splits, void *workspace, size_t workspace_bytes, void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, 1, Nk, d, scale);
+    if (s != FA_OK) return s;
+    if ((s = check_fwd_ptrs(q, k_cache, v_cache, o, lse, B, 1, Nk)) != FA_OK) return s;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
+    const int splits = fa_decode_splits(B, H, Hkv, Nk, num_splits);
+    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const long long blocks = (long long)splits * B * Hkv * ((H / Hkv + 15) / 16);
+    if (blocks > kMaxSlice) return FA_ERR_SHAPE;
+    if (B == 0) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::DecodeProblem p{};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nk = Nk; p.d = d; p.scale = scale; p.dtype = (int)dtype;
+    p.splits = splits;
+    p.chunk = decode_chunk(Nk, splits);
+    const size_t rows = (size_t)B * H * splits;
+    p.part_o = static_cast<float *>(workspace);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           (((rows * d * sizeof(float)) + 255) & ~(size_t)255));
+    return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n, void *stream)
+{
+    if (n == 0) return FA_OK;
+    if (!x) return FA_ERR_NULL;
+    if (n > (size_t)kMaxSlice * 256) return FA_ERR_SHAPE;
+    fa_status s = device_status();
+    if (s != FA_OK) return s;
+    return hip_status(fa::launch_cast_e4m3(x, codes, back, n, static_cast<hipStream_t>(stream)));
+}
+
+const char *fa_status_str(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size, H/Hkv < 1, or a tensor slice too large";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_GQA: return "FA_ERR_GQA: H must be a multiple of Hkv";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype not supported by this entry point";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0 (p_scale also <= 448)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace is NULL or too small";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE: the current device is not gfx950";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
+    case FA_ERR_ARG: return "FA_ERR_ARG: an argument is out of range";
+    }
+    return "unknown fa_status";
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// fa_device.hpp -- gfx950 device helpers shared by the kernels: vector types,
+// MFMA wrappers and small wave-level utilities.
+//
+// MFMA operand layouts used throughout (wave64):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A is 32(M) x 16(K), lane l holds row l%32
+//   and 8 K-values of group l/32; B is 16(K) x 32(N), lane l holds column
+//   l%32 and the same 8 K-values of group l/32; the 32x32 fp32 result holds,
+//   in lane l and register r, element (row 8*(r/4) + 4*(l/32) + r%4,
+//   column l%32).
+//   v_mfma_f32_16x16x32_{bf16,f16}: A 16x32, lane l holds row l%16 and the 8
+//   K-values of group l/16; B likewise by column; the 16x16 result holds, in
+//   lane l and register r, element (row 4*(l/16) + r, column l%16).
+//   v_mfma_f32_32x32x2f32: A 32x2, lane l holds A[l%32][l/32]; B 2x32, lane
+//   l holds B[l/32][l%32]; result as for 32x32x16.
+// A contraction only needs A and B to agree on which K index each
+// (lane group, element) slot carries, so the kernels choose the slot->K map
+// that makes their loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Native vector integers for raw 8/16-byte moves (HIP's uint4 is a union
+// struct whose copies can defeat register promotion).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-bit element traits: storage type, 8-wide MFMA operand type and the two
+// MFMA shapes used by the kernels.
+template <typename T> struct Mma16;
+
+template <> struct Mma16<__bf16> {
+    using v8 = bf16x8_t;
+    static __device__ __forceinline__ f32x16_t mma32(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma16<_Float16> {
+    using v8 = f16x8_t;
+    static __device__ __forceinline__ f32x16_t mma32(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t mma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From &x) {
+    static_assert(sizeof(To) == sizeof(From), "bitcast size");
+    return __builtin_bit_cast(To, x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack the low (resp. high) 16-bit halves of two dwords: result.lo = a.half,
+// result.hi = b.half.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+    return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+}  // namespace fa

@@ -1,0 +1,54 @@
+// fa_internal.hpp -- launcher interface between the C ABI (fa_api.cpp) and the
+// gfx950 kernels.  Arguments are validated by the caller before any launcher
+// runs; launchers only compute grids and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Forward (prefill) problem.  dtype: 0 = fp32, 1 = fp16, 2 = bf16.
+struct FwdProblem {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;  // nullable
+    int B, H, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+    int dtype;
+    // E4M3 P-cast variant (fp32 kernel only)
+    int pcast;
+    float p_scale;
+    int kv_reverse;
+    int n_sink;
+    unsigned long long *counts;  // nullable, 4 entries
+};
+
+struct DecodeProblem {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;  // nullable
+    int B, H, Hkv, Nk, d;
+    float scale;
+    int dtype;
+    int splits;  // resolved (>= 1)
+    int chunk;   // keys per split, multiple of kDecodeStep
+    float *part_o;    // [B, H, splits, d]
+    float *part_lse;  // [B, H, splits]
+};
+
+// Tile constants shared by the launchers and fa_kv_tile().
+constexpr int kFwdKvTile = 64;     // keys per KV tile, MFMA (bf16/fp16) kernel
+constexpr int kFwdQTile = 128;     // queries per workgroup (4 waves x 32)
+constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
+
+int fwd_f32_kv_tile(int d);  // keys per KV tile, fp32 / P-cast kernel
+hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);
+hipError_t launch_decode(const DecodeProblem &p, hipStream_t stream);
+hipError_t launch_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n,
+                            hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,163 @@
+/*
+ * fa.h -- C ABI of libfa: exact, IO-aware attention for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed.  O = softmax(Q K^T * scale) V, exactly (the result of the
+ * definition, up to floating-point rounding), tile by tile with the online
+ * softmax recurrence so the N x N score matrix never reaches device memory:
+ *   - marketmaker.cc blog "Atencion flash y la pregunta sobre la longitud de la
+ *     secuencia", sections "El algoritmo de atencion flash" (tiling, running
+ *     max m, running sum l, rescaled output accumulator), "La recurrencia de
+ *     softmax en linea" (a reassociation, not an approximation), "FA2:
+ *     paralelismo" (deferred normalisation, query-block parallelism, no
+ *     cross-wave row reductions) and "El enmascaramiento causal ..." (tiles
+ *     wholly in the future are neither loaded nor computed);
+ *   - systems-analysis.info "FlashAttention (IT)", section "Innovazioni chiave"
+ *     (tiling, online softmax, one fused kernel that writes only the output).
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no pointer after a call returns.
+ *   - Layout is contiguous row-major [batch, heads, seq, head_dim]:
+ *     q, o: [B, H, Nq, d];  k, v: [B, Hkv, Nk, d];  lse: [B, H, Nq] fp32.
+ *     o has the input dtype.  Tensor pointers must be 16-byte aligned.
+ *   - GQA/MQA: H must be a multiple of Hkv; query head h reads KV head
+ *     h / (H / Hkv) (shared KV heads as in gist.science "FlashAttention for
+ *     Scalable Vector Architectures", section "Metodologia").
+ *   - Causal masking is bottom-right aligned: key j is visible to query i
+ *     iff j <= i + (Nk - Nq).  A query with no visible key gets O = 0 and
+ *     LSE = -inf.
+ *   - lse holds the natural-log log-sum-exp of each score row,
+ *     LSE = m + ln(l), the O(N) statistics the backward pass keeps
+ *     (marketmaker.cc, section "Pase hacia atras").
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream).  No host synchronisation.
+ *   - Errors: arguments are validated on the host before any launch; on an
+ *     error nothing is launched and nothing is written.  There is never a
+ *     silent fallback to another algorithm (the warning of marketmaker.cc,
+ *     section "La integracion es de ocho lineas").  Launch failures return
+ *     FA_ERR_HIP.  A current device that is not gfx950 returns
+ *     FA_ERR_DEVICE.
+ *   - Empty work: B == 0 or Nq == 0 returns FA_OK without a launch.  The
+ *     pointer of an empty tensor may be NULL (q/o/lse when B*Nq == 0, k/v
+ *     when B*Nk == 0).  Nk == 0 with Nq > 0 writes O = 0 and LSE = -inf.
+ *   - Sizes: every tensor's element count per (batch, head) slice must be
+ *     below 2^31.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    FA_ERR_SHAPE = 2,     /* negative size, H or Hkv < 1, or a slice too large   */
+    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                  */
+    FA_ERR_GQA = 4,       /* H is not a multiple of Hkv                          */
+    FA_ERR_DTYPE = 5,     /* dtype not supported by this entry point            */
+    FA_ERR_ALIGN = 6,     /* a tensor pointer is not 16-byte aligned             */
+    FA_ERR_SCALE = 7,     /* scale or p_scale is not finite and > 0              */
+    FA_ERR_WORKSPACE = 8, /* decode workspace NULL or too small                  */
+    FA_ERR_DEVICE = 9,    /* current device is not gfx950 (or cannot be queried) */
+    FA_ERR_HIP = 10,      /* a kernel launch failed                              */
+    FA_ERR_ARG = 11       /* another argument out of range                       */
+} fa_status;
+
+/*
+ * Prefill / forward attention.
+ *   q, k, v : device inputs, layout above, element type `dtype`
+ *             (FA_BF16 and FA_F16 run on bf16/fp16 MFMA with fp32
+ *             accumulation; FA_F32 runs on fp32 MFMA).
+ *   o       : device output [B, H, Nq, d], same dtype as the inputs.
+ *   lse     : device output [B, H, Nq] fp32, or NULL to skip it.
+ *   causal  : 0 = full attention, 1 = bottom-right causal mask.
+ *   scale   : multiplier of Q K^T (normally 1/sqrt(d)); finite and > 0.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                 fa_dtype dtype, void *stream);
+
+/*
+ * Forward attention with the softmax probabilities cast to E4M3 before the
+ * P*V product (gist.science "Resumen Tecnico: Precision de P-Cast en la
+ * Atencion FP8", sections "Planteamiento del Problema", "Optimizacion 1" and
+ * "Optimizacion 2"): per KV tile, P = exp(s - m) relative to the RUNNING max
+ * m, then P~ = E4M3_RNE(p_scale * P) (OCP E4M3FN), O accumulates P~ V in
+ * fp32, the running sum l uses the uncast P, and the epilogue divides by
+ * p_scale * l.  Q, K, V stay fp32 (section "Contribuciones Clave", item 4).
+ *   dtype      : FA_F32 only.
+ *   p_scale    : the static scale S (256 recommended); finite, > 0, <= 448.
+ *   kv_reverse : 0 = KV tiles in increasing key order, 1 = decreasing
+ *                (the sink block last).
+ *   n_sink     : keys [0, n_sink) are sink keys, excluded from counts[0..1].
+ *   counts     : NULL, or a device array of 4 uint64 to which the call ADDS
+ *                (the caller initialises it):
+ *                [0] casts of non-sink keys (key >= n_sink),
+ *                [1] of those, values flushed to zero (P~ == 0 while P > 0),
+ *                [2] casts of keys outside the KV tiles that hold a sink key,
+ *                [3] of those, values flushed to zero.
+ *                Only visible (query, key) pairs with query < Nq count.
+ * The KV tile width that fixes the tile boundaries is fa_kv_tile(FA_F32, d, 1).
+ */
+fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                       fa_dtype dtype, float p_scale, int kv_reverse, int n_sink,
+                       unsigned long long *counts, void *stream);
+
+/* Keys per KV tile used by the forward kernels for (dtype, d, pcast), or -1
+ * for an unsupported combination.  Tile t covers keys [t*B_c, (t+1)*B_c). */
+int fa_kv_tile(fa_dtype dtype, int d, int pcast);
+
+/*
+ * Split-KV decode of one new query token per (batch, head) against a KV
+ * cache, merged with log-sum-exp.  The online recurrence is associative, so
+ * each split produces (O_s, lse_s) over its slice of keys and the merge is
+ *   LSE = M + ln sum_s exp(lse_s - M),  M = max_s lse_s,
+ *   O   = sum_s exp(lse_s - LSE) * O_s.
+ * Each workgroup serves every query head of one KV head from one read of
+ * its K/V slice (GQA: load the shared KV head once, gist.science
+ * "FlashAttention for Scalable Vector Architectures", section "Metodologia").
+ *   q        : device [B, H, 1, d];  k_cache, v_cache: device [B, Hkv, Nk, d].
+ *   o        : device [B, H, 1, d] (dtype);  lse: device [B, H, 1] fp32 or NULL.
+ *   No mask: the new token's K/V are already in the cache.
+ *   dtype    : FA_BF16 or FA_F16.
+ *   num_splits: 0 = automatic (fa_decode_splits), else 1..4096.
+ *   workspace: device scratch of at least
+ *              fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits) bytes,
+ *              16-byte aligned, owned by the caller; contents on entry do not
+ *              matter; two calls in flight must not share it.
+ */
+int fa_decode_splits(int B, int H, int Hkv, int Nk, int num_splits);
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits);
+fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                    float *lse, int B, int H, int Hkv, int Nk, int d, float scale,
+                    fa_dtype dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * The device E4M3 round trip that fa_fwd_pcast applies to p_scale * P, on n
+ * fp32 values: codes[i] = E4M3_RNE(x[i]) (OCP E4M3FN bit pattern),
+ * back[i] = the value of that code.  x, codes, back are device pointers
+ * (codes and back may each be NULL).  Exposed so the conversion can be
+ * checked against a reference codec.
+ */
+fa_status fa_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n, void *stream);
+
+const char *fa_status_str(fa_status s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: libfa.so loads, exports every function include/fa.h
+declares, and rejects bad arguments on the host before anything is launched.
+
+No test here launches a kernel: every call either fails validation (so no
+pointer is touched) or is an empty problem that returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_08_amd as fa
+from exact_io_aware_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000       # a 16-byte aligned fake address, never dereferenced
+PM = 0x10008      # misaligned fake address
+F32, F16, BF16 = 0, 1, 2
+S = {n: v for v, n in _lib.STATUS_NAMES.items()}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings_and_version():
+    lib = fa.load()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_str(code).decode().startswith(name)
+    assert lib.fa_status_str(99).decode() == "unknown fa_status"
+    assert fa.version() == 100
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=1, Nq=8, Nk=8, d=64, causal=1,
+             scale=0.125, dtype=BF16, stream=None)
+    a.update(kw)
+    return fa.load().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), "FA_ERR_NULL"), (dict(o=None), "FA_ERR_NULL"), (dict(v=None), "FA_ERR_NULL"),
+    (dict(k=PM), "FA_ERR_ALIGN"), (dict(lse=PM), "FA_ERR_ALIGN"),
+    (dict(B=-1), "FA_ERR_SHAPE"), (dict(H=0), "FA_ERR_SHAPE"), (dict(Hkv=0), "FA_ERR_SHAPE"),
+    (dict(Nq=-3), "FA_ERR_SHAPE"), (dict(Nk=-1), "FA_ERR_SHAPE"),
+    (dict(Nq=(1 << 31) // 64), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_HEADDIM"), (dict(d=256), "FA_ERR_HEADDIM"),
+    (dict(H=3, Hkv=2), "FA_ERR_GQA"),
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(scale=0.0), "FA_ERR_SCALE"), (dict(scale=-1.0), "FA_ERR_SCALE"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"), (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(causal=2), "FA_ERR_ARG"),
+    (dict(B=0), "FA_OK"), (dict(Nq=0), "FA_OK"),
+])
+def test_fwd_validation(kw, expect):
+    assert _fwd(**kw) == S[expect]
+
+
+def _pcast(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=2, Nq=8, Nk=8, d=128, causal=1,
+             scale=0.088, dtype=F32, p_scale=256.0, rev=1, n_sink=4, counts=P)
+    a.update(kw)
+    return fa.load().fa_fwd_pcast(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                  a["dtype"], a["p_scale"], a["rev"], a["n_sink"], a["counts"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), "FA_ERR_NULL"), (dict(counts=0x10004), "FA_ERR_ALIGN"),
+    (dict(dtype=BF16), "FA_ERR_DTYPE"), (dict(dtype=F16), "FA_ERR_DTYPE"),
+    (dict(p_scale=0.0), "FA_ERR_SCALE"), (dict(p_scale=512.0), "FA_ERR_SCALE"),
+    (dict(rev=2), "FA_ERR_ARG"), (dict(n_sink=-1), "FA_ERR_ARG"),
+    (dict(d=32), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
+])
+def test_pcast_validation(kw, expect):
+    assert _pcast(**kw) == S[expect]
+
+
+def _decode(ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, Hkv=2, Nk=100, d=64, scale=0.125,
+             dtype=BF16, splits=0, ws=P)
+    a.update(kw)
+    need = fa.decode_workspace_bytes(a["B"], a["H"], a["Hkv"], a["Nk"], a["d"], a["splits"])
+    return fa.load().fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                               a["Hkv"], a["Nk"], a["d"], a["scale"], a["dtype"], a["splits"],
+                               a["ws"], need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=None), "FA_ERR_NULL"), (dict(ws=None), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes=16), "FA_ERR_WORKSPACE"), (dict(ws=PM), "FA_ERR_ALIGN"),
+    (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(splits=-1), "FA_ERR_ARG"),
+    (dict(splits=5000), "FA_ERR_ARG"), (dict(H=6, Hkv=4), "FA_ERR_GQA"),
+    (dict(d=80), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
+])
+def test_decode_validation(kw, expect):
+    assert _decode(**kw) == S[expect]
+
+
+def test_decode_split_policy_and_workspace():
+    # automatic split count: about 1024 workgroups, no split under 256 keys
+    assert fa.decode_splits(16, 32, 4, 8192) == 16
+    assert fa.decode_splits(1, 8, 8, 100) == 1
+    assert fa.decode_splits(1, 8, 1, 1 << 20) == 1024
+    assert fa.decode_splits(2, 8, 2, 100, num_splits=7) == 7
+    assert fa.decode_splits(2, 8, 3, 100) == -1
+    ws = fa.decode_workspace_bytes(16, 32, 4, 8192, 64)
+    rows = 16 * 32 * 16
+    assert ws >= rows * 64 * 4 + rows * 4
+    assert fa.decode_workspace_bytes(1, 1, 1, 10, 96) == 0
+
+
+def test_kv_tile_and_cast_validation():
+    assert fa.kv_tile(__import__("torch").bfloat16, 64) == 64
+    lib = fa.load()
+    assert lib.fa_kv_tile(F32, 128, 1) in (32, 64)
+    assert lib.fa_kv_tile(BF16, 64, 1) == -1
+    assert lib.fa_kv_tile(F32, 48, 0) == -1
+    assert lib.fa_cast_e4m3(None, None, None, 4, None) == S["FA_ERR_NULL"]
+    assert lib.fa_cast_e4m3(None, None, None, 0, None) == S["FA_OK"]
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)

@@ -1,0 +1,95 @@
+"""GPU parity of fa_decode (split-KV GQA decode + LSE merge) against the fp64
+oracle (the definition with one query row and every key visible)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_08_amd as fa
+import fagen
+import oracle
+from gpu_util import announce, compare, need_gpu, to_dev, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(B, H, Hkv, Nk, d, dt, splits=0, seed=0, poison_ws=False):
+    need_gpu()
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    announce(f"fa_decode B={B} H={H} Hkv={Hkv} Nk={Nk} d={d} {dt} splits={splits} seed={seed}")
+    cfg = dict(B=B, H=H, Hkv=Hkv, Nq=1, Nk=Nk, d=d, dtype=dt, kind="iid")
+    q, k, v = fagen.make_inputs(cfg, seed)
+    ws = None
+    if poison_ws:
+        nb = fa.decode_workspace_bytes(B, H, Hkv, Nk, d, splits)
+        ws = torch.full((nb // 4,), float("nan"), device="cuda").view(torch.uint8)
+    o, lse = fa.decode(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), scale=scale,
+                       num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(widen(q, dt), widen(k, dt), widen(v, dt), False, scale)
+    return compare(o, lse, o_ref, lse_ref, dt, "decode")
+
+
+def test_tinyllama_gqa_decode_bf16():
+    """B=16, 32 query heads / 4 KV heads, Nk=8192, d=64, bf16 (automatic split)."""
+    assert fa.decode_splits(16, 32, 4, 8192) == 16
+    run_decode(16, 32, 4, 8192, 64, "bf16")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16, 64])
+def test_split_counts(splits):
+    run_decode(2, 8, 2, 3000, 64, "bf16", splits=splits, seed=splits, poison_ws=True)
+
+
+@pytest.mark.parametrize("Nk", [1, 100, 129, 1000, 8191])
+def test_ragged_cache_lengths(Nk):
+    run_decode(3, 8, 2, Nk, 64, "bf16", seed=Nk)
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 1), (40, 2), (32, 1)])
+def test_group_sizes(H, Hkv):
+    """MHA, MQA, and groups wider than 16 heads (two query groups per KV head)."""
+    run_decode(2, H, Hkv, 777, 64, "bf16", seed=H + Hkv)
+
+
+@pytest.mark.parametrize("dt,d", [("f16", 64), ("bf16", 128), ("f16", 128)])
+def test_dtypes_and_head_dims(dt, d):
+    run_decode(4, 16, 4, 2048, d, dt, seed=d)
+
+
+def test_empty_cache():
+    need_gpu()
+    announce("fa_decode Nk=0")
+    q = torch.randn(2, 4, 1, 64, device="cuda").to(torch.bfloat16)
+    kv = torch.empty(2, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = fa.decode(q, kv, kv)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_decode_equals_last_causal_prefill_row():
+    need_gpu()
+    announce("fa_decode vs fa_fwd last causal row, N=1500")
+    cfg = dict(B=2, H=8, Hkv=2, Nq=1500, Nk=1500, d=64, dtype="bf16", kind="iid")
+    q, k, v = fagen.make_inputs(cfg, 11)
+    dq, dk, dv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o_full, l_full = fa.fwd(dq, dk, dv, causal=True)
+    o_dec, l_dec = fa.decode(dq[:, :, -1:].contiguous(), dk, dv)
+    torch.cuda.synchronize()
+    diff = (o_full[:, :, -1:].float() - o_dec.float()).abs().max().item()
+    assert diff <= 2e-2
+    assert (l_full[:, :, -1:] - l_dec).abs().max().item() <= 1e-3
+
+
+def test_determinism():
+    need_gpu()
+    announce("fa_decode determinism")
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q = torch.randn(4, 16, 1, 64, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(4, 2, 5000, 64, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(4, 2, 5000, 64, device="cuda", generator=g).to(torch.bfloat16)
+    o1, l1 = fa.decode(q, k, v)
+    o2, l2 = fa.decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
