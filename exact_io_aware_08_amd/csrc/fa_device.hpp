@@ -30,6 +30,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // struct whose copies can defeat register promotion).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -65,13 +66,34 @@ __device__ __forceinline__ To bitcast(const From &x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Registers loaded once before a loop (e.g. the Q operand): pass them
+// through an empty asm that redefines them.  The wait for their loads then
+// happens here, once, and the loop body does not have to drain in-flight
+// prefetches before each use.
+template <typename V, int N>
+__device__ __forceinline__ void settle(V (&r)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// Workgroup barrier that orders LDS traffic only: it waits for this wave's
+// LDS operations, not for outstanding global loads (which only fill
+// registers), so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Pack the low (resp. high) 16-bit halves of two dwords: result.lo = a.half,
 // result.hi = b.half.
+// (v_perm_b32 byte selects: 0-3 pick bytes of the second operand, 4-7 of
+// the first.)
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
-    return (a & 0xFFFFu) | (b << 16);
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xFFFF0000u);
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 }  // namespace fa

@@ -4,28 +4,44 @@
 // de la secuencia", sections "El algoritmo de atencion flash" (Q split into
 // row blocks, K/V into column blocks, each query block sweeps the KV blocks
 // keeping a running max m, running sum l and an output accumulator) and
-// "La recurrencia de softmax en linea" (accumulator rescaled by
-// e^(m_old - m_new) whenever the max grows); "FA2: paralelismo" (the
-// normalisation by l is deferred to the end; the grid also runs over query
-// blocks; each wave owns whole query rows, so no cross-wave reduction);
-// "El enmascaramiento causal ..." (KV tiles wholly in the future are never
-// loaded or computed).  systems-analysis.info "FlashAttention (IT)",
-// "Innovazioni chiave": QK^T, mask, softmax and xV fused in one kernel that
-// writes only O (and the per-row LSE).
+// "La recurrencia de softmax en linea" (the accumulator is rescaled by
+// e^(m_old - m_new) when the reference max grows; the result is a
+// reassociation of the two-pass softmax); "FA2: paralelismo" (normalisation
+// deferred to the end; the grid also runs over query blocks; each wave owns
+// whole query rows); "FA3: Mecanica de la tolva", item 2 (the score matmul of
+// one block runs while the softmax of the previous block runs on the other
+// unit); "El enmascaramiento causal ..." (KV tiles wholly in the future are
+// never loaded or computed).  systems-analysis.info "FlashAttention (IT)",
+// "Innovazioni chiave": one fused kernel that writes only O (and the LSE).
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows of one (b, h)):
-//  * Each wave owns 32 query rows.  Scores are computed transposed,
-//    S^T = K Q^T, on v_mfma_f32_32x32x16: the fp32 result then gives lane l
-//    the 16 keys {8i + 4(l/32) + r} of query l%32, so a row's max needs one
-//    exchange between lanes l and l^32 and its sum none until the epilogue.
-//  * The S^T accumulator is directly the B operand of O^T = V^T P^T (after a
-//    cvt to bf16/fp16): key-slot k of lane group g in K-step t is key
-//    16t + 8(k/4) + 4g + k%4 of the 32-key block.  V^T is therefore staged
-//    in LDS transposed ([d][key]) so the A operand is two 8-byte reads.
-//  * K tiles are staged row-major in LDS ([key][d], padded), read as 16-byte
-//    A-operand rows.  Q stays in registers for the whole sweep.
-//  * Global loads of KV tile j+1 are issued before tile j is computed, so
-//    HBM/L2 latency overlaps the MFMA and softmax work.
+// gfx950 mapping (one workgroup = 4 waves; each wave owns QB blocks of 32
+// query rows of one (b, h); a KV tile has NKB blocks of 32 keys, QB*NKB = 2):
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16:
+//    the fp32 result gives lane l the 16 keys {8i + 4(l/32) + r} of query
+//    l%32 per 32x32 block, so a row's max needs one v_permlane32_swap and
+//    its sum no exchange until the epilogue.
+//  * The S^T accumulator is directly the B operand of O^T = V^T P^T (after
+//    v_cvt_pk to bf16/fp16): key-slot k of lane group g in K-step t is key
+//    16t + 8(k/4) + 4g + k%4 of the 32-key block.  V^T is staged in LDS
+//    transposed ([d][key]) so the A operand is two 8-byte reads; K is staged
+//    row-major ([key][d]) and read as 16-byte A-operand rows.  Q stays in
+//    registers for the whole sweep.
+//  * Every K and V^T operand read from LDS feeds all QB query blocks of the
+//    wave, so LDS traffic per MFMA falls as QB grows (QB = 2 at d = 64,
+//    where it is what bounds the loop; QB = 1 at d = 128 for registers).
+//  * Pipeline with one barrier per KV tile: K is staged one tile ahead of V
+//    (both double-buffered in LDS) and global loads run two tiles ahead, so
+//    in iteration j the wave issues the S^T MFMAs of tile j+1 interleaved
+//    with the softmax of tile j on the VALU, then the P V MFMAs of tile j
+//    interleaved with staging the next tiles.
+//  * Global loads are buffer loads with the descriptor rebased per tile:
+//    rows past the end of a slice read as zero (hardware range check), so
+//    ragged tails need no address clamping on the VALU.
+//  * The reference max of each row is the exact max of its first tile; it
+//    is moved (with the e^(m_old - m_new) rescale) only when a later tile's
+//    exponentials leave a safe range, detected from that tile's row sums.
+//    In exact arithmetic any reference value gives the same O and LSE, and
+//    the per-tile row max and rescale stay off the common path.
 //  * Causal grids run the longest query tiles first.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
@@ -33,67 +49,127 @@
 namespace fa {
 namespace {
 
-constexpr int NW = 4;
-constexpr int BR = NW * 32;
-constexpr int BC = kFwdKvTile;
-static_assert(BR == kFwdQTile, "query tile");
-static_assert(BC == 64, "the kernel body assumes two 32-key blocks per tile");
+constexpr int NW = 4;         // waves per workgroup
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9 V# word 3)
 
-// Tile geometry of the KV staging (256 threads, 16-byte chunks).
-template <int D> struct KvGeom {
-    static constexpr int KSTR = D + 8;            // K tile row stride in LDS (elements)
-    static constexpr int VSTR = BC + 4;           // V^T tile row stride in LDS (elements)
-    static constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-    static constexpr int KCH = BC * CPR / 256;    // K chunks per thread per tile
-    static constexpr int PPR = 256 / CPR;         // V key pairs per round
-    static constexpr int VROUNDS = (BC / 2) / PPR;
-    static_assert(KCH * 256 == BC * CPR && VROUNDS * PPR * 2 == BC, "tile split");
+// Row-sum accumulation of one converted pair of probabilities.  For fp16
+// the sum is taken over the converted values with v_dot2 (an 11-bit
+// mantissa keeps the normaliser within 2^-12 relative); bf16 keeps only 8
+// bits, which would move the LSE by up to 2^-9, so its sum adds the fp32
+// values.
+template <typename T> struct Pack2;
+template <> struct Pack2<__bf16> {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ float add(v2, float p0, float p1, float c) {
+        return c + p0 + p1;
+    }
+};
+template <> struct Pack2<_Float16> {
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ float add(v2 a, float, float, float c) {
+        const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(a, one, c, false);
+    }
 };
 
-// Global -> registers for KV tile starting at key j0.  Keys past Nk (ragged
-// last tile) load row Nk-1 instead: their scores are masked to -inf, so they
-// get weight 0 and the finite V row adds nothing.
+// Geometry for head dim D and QB query blocks per wave.
+template <int D, int QB> struct Geo {
+    static constexpr int NKB = 2 / QB;           // 32-key blocks per KV tile
+    static constexpr int BC = 32 * NKB;          // keys per KV tile
+    static constexpr int BR = NW * 32 * QB;      // queries per workgroup
+    static constexpr int KSTR = D + 8;           // K tile row stride in LDS (elements)
+    static constexpr int VSTR = BC + 4;          // V^T tile row stride in LDS (elements)
+    static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+    static constexpr int KCH = BC * CPR / 256;   // K chunks per thread per tile
+    static constexpr int VPC = (BC / 2) * CPR;   // V (key pair, chunk) items per tile
+    static constexpr int VTH = VPC < 256 ? VPC : 256;  // threads staging V
+    static constexpr int VROUNDS = VPC / VTH;
+    static constexpr int PPR = VTH / CPR;        // key pairs per V round
+    static_assert(QB * NKB == 2, "two 32x32 score blocks per wave");
+    static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "K staging split");
+    static_assert(VTH % 64 == 0 && VROUNDS * VTH == VPC && PPR % 16 == 0, "V staging split");
+};
+
+// Buffer resource over rows [j0, rows) of a row-major slice of D-element
+// rows: loads past the end read as zero.  All arguments are wave-uniform.
 template <typename T, int D>
-__device__ __forceinline__ void load_kv_tile(const T *__restrict__ Kb, const T *__restrict__ Vb,
-                                             int Nk, int j0, int tid,
-                                             u32x4_t (&kreg)[KvGeom<D>::KCH],
-                                             u32x4_t (&vreg)[2 * KvGeom<D>::VROUNDS])
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int j0)
 {
-    using G = KvGeom<D>;
+    const int left = rows > j0 ? (rows - j0) * D * (int)sizeof(T) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0, left,
+                                             kBufferFlags);
+}
+
+// Per-thread offsets of the staging loads and LDS stores within a tile.
+//  K: chunk ci = tid + 256 r -> row ci / CPR, chunk ci % CPR (row-major,
+//     coalesced).
+//  V: threads tid < VTH; lane l of 32-lane group g handles key pair kp and
+//     chunk cc with kp = l % 16 + PPR r and cc = l / 16 + 2 g, so the 32
+//     dwords a half-wave writes into V^T land in 32 distinct banks.
+template <int D, int QB> struct KvMap {
+    using G = Geo<D, QB>;
+    int koff[G::KCH];      // byte offsets of the K chunks
+    int kst[G::KCH];       // LDS element offsets of the K chunks
+    int voff[G::VROUNDS];  // byte offset of key 2kp, chunk cc (key 2kp+1 is + D elements)
+    int vst[G::VROUNDS];   // LDS element offset of V^T[8cc][2kp]
+    __device__ __forceinline__ KvMap(int tid, int elem_bytes) {
 #pragma unroll
-    for (int r = 0; r < G::KCH; ++r) {
-        const int ci = tid + r * 256;
-        const int key = min(j0 + ci / G::CPR, Nk - 1), cc = ci % G::CPR;
-        kreg[r] = *reinterpret_cast<const u32x4_t *>(Kb + (size_t)key * D + cc * 8);
+        for (int r = 0; r < G::KCH; ++r) {
+            const int ci = tid + r * 256;
+            koff[r] = ((ci / G::CPR) * D + (ci % G::CPR) * 8) * elem_bytes;
+            kst[r] = (ci / G::CPR) * G::KSTR + (ci % G::CPR) * 8;
+        }
+        const int l = tid & 31, g = (tid >> 5) & (G::VTH / 32 - 1);
+#pragma unroll
+        for (int r = 0; r < G::VROUNDS; ++r) {
+            const int kp = (l & 15) + G::PPR * r;
+            const int cc = (l >> 4) + 2 * g;
+            voff[r] = ((2 * kp) * D + cc * 8) * elem_bytes;
+            vst[r] = (cc * 8) * G::VSTR + 2 * kp;
+        }
     }
+};
+
+template <typename T, int D, int QB>
+__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rs, const KvMap<D, QB> &mp,
+                                       u32x4_t (&kreg)[Geo<D, QB>::KCH])
+{
 #pragma unroll
-    for (int r = 0; r < G::VROUNDS; ++r) {
-        const int kp = tid / G::CPR + r * G::PPR, cc = tid % G::CPR;
-        const int k0 = min(j0 + 2 * kp, Nk - 1), k1 = min(j0 + 2 * kp + 1, Nk - 1);
-        vreg[2 * r] = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)k0 * D + cc * 8);
-        vreg[2 * r + 1] = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)k1 * D + cc * 8);
+    for (int r = 0; r < Geo<D, QB>::KCH; ++r)
+        kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.koff[r], 0, 0);
+}
+
+template <typename T, int D, int QB>
+__device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rs, const KvMap<D, QB> &mp,
+                                       u32x4_t (&vreg)[2 * Geo<D, QB>::VROUNDS])
+{
+#pragma unroll
+    for (int r = 0; r < Geo<D, QB>::VROUNDS; ++r) {
+        vreg[2 * r] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.voff[r], 0, 0);
+        vreg[2 * r + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.voff[r] + D * (int)sizeof(T), 0, 0);
     }
 }
 
-// Registers -> LDS: K row-major [key][d]; V transposed [d][key], two keys
-// packed per dword (key 2kp in the low half, 2kp+1 in the high half).
-template <typename T, int D>
-__device__ __forceinline__ void store_kv_tile(T *Ks, T *Vt, int tid,
-                                              const u32x4_t (&kreg)[KvGeom<D>::KCH],
-                                              const u32x4_t (&vreg)[2 * KvGeom<D>::VROUNDS])
+// Registers -> LDS: K row-major [key][d].
+template <typename T, int D, int QB>
+__device__ __forceinline__ void store_k(T *Ks, const KvMap<D, QB> &mp,
+                                        const u32x4_t (&kreg)[Geo<D, QB>::KCH])
 {
-    using G = KvGeom<D>;
 #pragma unroll
-    for (int r = 0; r < G::KCH; ++r) {
-        const int ci = tid + r * 256;
-        *reinterpret_cast<u32x4_t *>(&Ks[(ci / G::CPR) * G::KSTR + (ci % G::CPR) * 8]) = kreg[r];
-    }
+    for (int r = 0; r < Geo<D, QB>::KCH; ++r) *reinterpret_cast<u32x4_t *>(&Ks[mp.kst[r]]) = kreg[r];
+}
+
+// Registers -> LDS: V transposed [d][key], keys 2kp (low half) and 2kp+1
+// (high half) packed per dword.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void store_v(T *Vt, const KvMap<D, QB> &mp,
+                                        const u32x4_t (&vreg)[2 * Geo<D, QB>::VROUNDS])
+{
+    using G = Geo<D, QB>;
 #pragma unroll
     for (int r = 0; r < G::VROUNDS; ++r) {
-        const int kp = tid / G::CPR + r * G::PPR, cc = tid % G::CPR;
         const u32x4_t a = vreg[2 * r], bq = vreg[2 * r + 1];
-        // element e of the chunk is d = 8cc + e
-        uint32_t *base = reinterpret_cast<uint32_t *>(&Vt[(cc * 8) * G::VSTR + 2 * kp]);
+        uint32_t *base = reinterpret_cast<uint32_t *>(&Vt[mp.vst[r]]);
         constexpr int RS = G::VSTR / 2;  // V^T row stride in dwords
         base[0 * RS] = pack_lo16(a.x, bq.x);
         base[1 * RS] = pack_hi16(a.x, bq.x);
@@ -106,7 +182,41 @@ __device__ __forceinline__ void store_kv_tile(T *Ks, T *Vt, int tid,
     }
 }
 
-template <typename T, int D, bool CAUSAL>
+// S^T blocks (32 keys x 32 queries each) = K_tile Q_wave^T; block index
+// qb * NKB + kb.  Each K operand read serves all QB query blocks.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void scores(const T *Ks, const typename Mma16<T>::v8 (&qop)[QB][D / 16],
+                                       int c, int hh, f32x16_t (&s)[2])
+{
+    using M = Mma16<T>;
+    using v8 = typename M::v8;
+    using G = Geo<D, QB>;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s[i] = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            const v8 kop = *reinterpret_cast<const v8 *>(&Ks[(kb * 32 + c) * G::KSTR + 16 * t + 8 * hh]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb * G::NKB + kb] = M::mma32(kop, qop[qb][t], s[qb * G::NKB + kb]);
+        }
+}
+
+// Max / sum over the two lanes (l, l^32) that hold one query row.
+__device__ __forceinline__ float max_pair(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_pair(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int D, int QB, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                 T *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk,
@@ -114,16 +224,16 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 {
     using M = Mma16<T>;
     using v8 = typename M::v8;
-    constexpr int KSTR = KvGeom<D>::KSTR;
-    constexpr int VSTR = KvGeom<D>::VSTR;
-    constexpr int KCH = KvGeom<D>::KCH;
-    constexpr int VROUNDS = KvGeom<D>::VROUNDS;
+    using P2 = Pack2<T>;
+    using G = Geo<D, QB>;
+    constexpr int BC = G::BC, NKB = G::NKB, VSTR = G::VSTR;
 
-    __shared__ __attribute__((aligned(16))) T Ks[BC * KSTR];
-    __shared__ __attribute__((aligned(16))) T Vt[D * VSTR];
+    __shared__ __attribute__((aligned(16))) T Kbuf[2][BC * G::KSTR];
+    __shared__ __attribute__((aligned(16))) T Vbuf[2][D * VSTR];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, c = lane & 31, hh = lane >> 5;
+    const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
 
     const int qt = n_qtiles - 1 - (int)(blockIdx.x / (unsigned)n_bh);
     const int bh = (int)(blockIdx.x % (unsigned)n_bh);
@@ -136,142 +246,244 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     const T *Vb = V + kvoff;
     T *Ob = O + qoff;
 
-    const int q0 = qt * BR;
-    const int q0w = q0 + w * 32;
+    const int q0 = qt * G::BR;
+    const int q0w = q0 + w * 32 * QB;  // first row of this wave
     const int off = Nk - Nq;
     int nkt = (Nk + BC - 1) / BC;
     if (CAUSAL) {
-        const int lim = min(q0 + BR, Nq) - 1 + off;  // last key any row of the block sees
+        const int lim = min(q0 + G::BR, Nq) - 1 + off;  // last key any row of the block sees
         nkt = lim < 0 ? 0 : min(nkt, lim / BC + 1);
     }
 
-    // Q operand (B of S^T = K Q^T): lane (c, hh) holds Q[q0w + c][16t + 8hh + e].
-    // Rows past Nq load the last row instead; their results are never stored.
-    v8 qop[D / 16];
+    // Q operand (B of S^T = K Q^T): lane (c, hh) holds Q[q0w + 32qb + c][16t + 8hh + e].
+    // Rows past Nq read as zeros (buffer range check); they are never stored.
+    v8 qop[QB][D / 16];
     {
-        const int qrow = min(q0w + c, Nq - 1);
+        const __amdgpu_buffer_rsrc_t rq = rows_rsrc<T, D>(Qb, Nq, q0w);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-            qop[t] = bitcast<v8>(*reinterpret_cast<const u32x4_t *>(Qb + (size_t)qrow * D + 16 * t + 8 * hh));
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+                qop[qb][t] = bitcast<v8>(__builtin_amdgcn_raw_buffer_load_b128(
+                    rq, ((32 * qb + c) * D + 16 * t + 8 * hh) * (int)sizeof(T), 0, 0));
+            settle(qop[qb]);
+        }
     }
 
-    f32x16_t acc[D / 32];
+    f32x16_t acc[QB][D / 32];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[qb][i] = f32x16_t{};
+    float m_ref[QB], l_run[QB];  // reference max (raw units; same in lanes l, l^32), row-sum share
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_ref[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+    }
 
-    u32x4_t kreg[KCH], vreg[2 * VROUNDS];
-    if (nkt > 0) load_kv_tile<T, D>(Kb, Vb, Nk, 0, tid, kreg, vreg);
-    for (int j = 0; j < nkt; ++j) {
-        __syncthreads();  // every wave is done reading tile j-1
-        store_kv_tile<T, D>(Ks, Vt, tid, kreg, vreg);
-        __syncthreads();
-        if (j + 1 < nkt) load_kv_tile<T, D>(Kb, Vb, Nk, (j + 1) * BC, tid, kreg, vreg);
+    const KvMap<D, QB> mp(tid, (int)sizeof(T));
+    const bool stages_v = tid < G::VTH;  // wave-uniform
+    u32x4_t kreg[G::KCH], vreg[2 * G::VROUNDS];
+    f32x16_t s_a[2], s_b[2];
+    auto tile = [&](int jj) { return min(jj, nkt - 1) * BC; };  // clamped first key of a tile
+
+    if (nkt > 0) {
+        // prologue: K0 -> Kbuf[0], V0 -> Vbuf[0], K1 -> Kbuf[1]; registers
+        // then hold K2 and V1.
+        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, 0), mp, kreg);
+        if (stages_v) load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, 0), mp, vreg);
+        store_k<T, D, QB>(Kbuf[0], mp, kreg);
+        if (stages_v) store_v<T, D, QB>(Vbuf[0], mp, vreg);
+        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(1)), mp, kreg);
+        if (stages_v) load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(1)), mp, vreg);
+        store_k<T, D, QB>(Kbuf[1], mp, kreg);
+        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(2)), mp, kreg);
+        lds_barrier();
+        scores<T, D, QB>(Kbuf[0], qop, c, hh, s_a);
+        lds_barrier();  // Kbuf[0] is overwritten in iteration 0
+    }
+
+    // One KV tile.  Invariant on entry: sc = S^T of tile j; Kbuf[(j+1)&1] =
+    // K_{j+1}; Vbuf[j&1] = V_j; kreg = K_{j+2}; vreg = V_{j+1} (tile indices
+    // past the last tile are clamped to it; those copies go to buffers that
+    // are never read again).  The staging is branch-free apart from the
+    // wave-uniform choice of which waves stage V, so the only waits on
+    // global loads are for data requested a full tile earlier.  Tiles past
+    // a wave's causal limit are processed fully masked (weight 0), which
+    // keeps the hot blocks free of branches so the scheduler can interleave
+    // MFMA and VALU instructions within the wave.
+    auto step = [&](int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         const int j0 = j * BC;
-        if (CAUSAL && j0 > q0w + 31 + off) continue;  // no row of this wave sees tile j
-
-        // ---- S^T = K_j Q^T (fp32) ----
-        f32x16_t s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16_t{};
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t) {
-                const v8 kop = *reinterpret_cast<const v8 *>(&Ks[(kb * 32 + c) * KSTR + 16 * t + 8 * hh]);
-                s[kb] = M::mma32(kop, qop[t], s[kb]);
-            }
-        }
-
-        // ---- mask: ragged last tile, and the diagonal band when causal ----
+        // ---- mask: ragged last tile, the diagonal band and beyond (causal) ----
         const bool need_mask = (j0 + BC > Nk) || (CAUSAL && j0 + BC - 1 > q0w + off);
         if (need_mask) {
-            const int lim = CAUSAL ? min(Nk, q0w + c + off + 1) : Nk;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                const int lim = CAUSAL ? min(Nk, q0w + 32 * qb + c + off + 1) : Nk;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= lim) s[kb][r] = -INFINITY;
-                }
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        if (key >= lim) sc[qb * NKB + kb][r] = -INFINITY;
+                    }
+            }
         }
 
-        // ---- online softmax (running max; normalisation deferred) ----
-        float mx = -INFINITY;
+        // ---- reference max ----
+        // Set from the exact row max on the first tile (and for rows that
+        // have not seen a key yet).  Afterwards it is only moved when a
+        // tile's exponentials leave the safe range, which the row sums below
+        // detect; the per-tile row max is then never computed on the common
+        // path.  Any finite reference gives the same O and LSE.
+        auto rebase = [&]() {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                float m = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-        const float mneg = -m_use * scale_log2;
-        float rs = 0.f;
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+                    for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb * NKB + kb][r]);
+                m = max_pair(m);
+                // alpha = 1 on rows that keep their reference (including rows
+                // still without any visible key); 0 when the old one was -inf.
+                const bool raise = m > m_ref[qb];
+                const float alpha = raise ? fast_exp2((m_ref[qb] - m) * scale_log2) : 1.f;
+                m_ref[qb] = raise ? m : m_ref[qb];
+                l_run[qb] *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[kb][r], scale_log2, mneg));
-                s[kb][r] = p;
-                rs += p;
+                for (int i = 0; i < D / 32; ++i) acc[qb][i] *= alpha;
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+        };
+        bool fresh = (j == 0);
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        for (int qb = 0; qb < QB; ++qb) fresh |= (m_ref[qb] == -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(fresh) != 0) rebase();
 
-        // ---- O^T += V_j^T P^T ----
-        v8 pop[4];
+        // P = exp2(s*c - m*c) packed to 16-bit, with this tile's row sums.
+        v8 pop[2][2];  // [score block][K-step]
+        float ts[QB];
+        auto make_p = [&]() {
+            float mneg[QB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                mneg[qb] = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb] * scale_log2;
+                ts[qb] = 0.f;
+            }
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pop[kb * 2 + t][e] = static_cast<T>(s[kb][8 * t + e]);
+                for (int t = 0; t < 2; ++t) {
+                    const int qb = sb / NKB;
+                    typename P2::v2 pk[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = fast_exp2(fmaf(sc[sb][8 * t + 2 * e], scale_log2, mneg[qb]));
+                        const float p1 = fast_exp2(fmaf(sc[sb][8 * t + 2 * e + 1], scale_log2, mneg[qb]));
+                        pk[e] = __builtin_convertvector((f32x2_t{p0, p1}), typename P2::v2);
+                        ts[qb] = P2::add(pk[e], p0, p1, ts[qb]);
+                    }
+                    pop[sb][t] = bitcast<v8>(u32x4_t{bitcast<uint32_t>(pk[0]), bitcast<uint32_t>(pk[1]),
+                                                     bitcast<uint32_t>(pk[2]), bitcast<uint32_t>(pk[3])});
+                }
+        };
+
+        // ---- hot block 1: S^T of tile j+1 on the MFMA pipe while the VALU
+        //      turns tile j into P (exp2, cvt to 16-bit, row sums) ----
+        scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, sn);
+        make_p();
+        constexpr int N_S_MFMA = 2 * (D / 16);
+        __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (D / 16), 0);  // K operand LDS reads
+#pragma unroll
+        for (int i = 0; i < N_S_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x0002, 96 / N_S_MFMA, 0);   // VALU
+        }
+
+        // Range check: exponentials above 2^64 per tile (or inf/NaN) mean the
+        // reference is far below this tile's scores; rebase and redo the tile.
+        bool out_of_range = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) out_of_range |= !(ts[qb] < 0x1p64f);
+        if (__builtin_amdgcn_ballot_w64(out_of_range) != 0) {
+            rebase();
+            make_p();
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += ts[qb];
+
+        // ---- hot block 2: O^T += V_j^T P^T, interleaved with staging the
+        //      next tiles into the LDS buffers not read in this step ----
+        const T *Vt = Vbuf[j & 1];
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const T *vp = &Vt[(32 * mb + c) * VSTR + kb * 32 + 16 * t + 4 * hh];
                     const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vp);
                     const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vp + 8);
                     const v8 vop = bitcast<v8>(u32x4_t{lo.x, lo.y, hi.x, hi.y});
-                    acc[mb] = M::mma32(vop, pop[kb * 2 + t], acc[mb]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        acc[qb][mb] = M::mma32(vop, pop[qb * NKB + kb][t], acc[qb][mb]);
                 }
+        store_k<T, D, QB>(Kbuf[j & 1], mp, kreg);
+        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(j + 3)), mp, kreg);
+        if (stages_v) {
+            store_v<T, D, QB>(Vbuf[(j + 1) & 1], mp, vreg);
+            load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(j + 2)), mp, vreg);
+        }
+        lds_barrier();
+    };
+
+    // Unrolled by two so the score registers swap roles instead of being copied.
+    for (int j = 0; j < nkt; j += 2) {
+        step(j, s_a, s_b);
+        if (j + 1 < nkt) step(j + 1, s_b, s_a);
     }
 
     // ---- epilogue: O = acc / l, LSE = m*scale + ln l ----
-    const float l = l_run + __shfl_xor(l_run, 32);
-    const int row = q0w + c;
-    if (row < Nq) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l = sum_pair(l_run[qb]);
+        const int row = q0w + 32 * qb + c;
+        if (row < Nq) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * mb + 8 * i + 4 * hh;
-                typedef T t4 __attribute__((ext_vector_type(4)));
-                t4 vals;
-                vals[0] = static_cast<T>(acc[mb][4 * i + 0] * inv);
-                vals[1] = static_cast<T>(acc[mb][4 * i + 1] * inv);
-                vals[2] = static_cast<T>(acc[mb][4 * i + 2] * inv);
-                vals[3] = static_cast<T>(acc[mb][4 * i + 3] * inv);
-                *reinterpret_cast<t4 *>(Ob + (size_t)row * D + d0) = vals;
-            }
-        if (LSE != nullptr && hh == 0)
-            LSE[(size_t)bh * Nq + row] = l > 0.f ? m_run * scale + logf(l) : -INFINITY;
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d0 = 32 * mb + 8 * i + 4 * hh;
+                    t4 vals;
+                    vals[0] = static_cast<T>(acc[qb][mb][4 * i + 0] * inv);
+                    vals[1] = static_cast<T>(acc[qb][mb][4 * i + 1] * inv);
+                    vals[2] = static_cast<T>(acc[qb][mb][4 * i + 2] * inv);
+                    vals[3] = static_cast<T>(acc[qb][mb][4 * i + 3] * inv);
+                    *reinterpret_cast<t4 *>(Ob + (size_t)row * D + d0) = vals;
+                }
+            if (LSE != nullptr && hh == 0)
+                LSE[(size_t)bh * Nq + row] = l > 0.f ? m_ref[qb] * scale + logf(l) : -INFINITY;
+        }
     }
 }
+
+// Query blocks per wave: two at d = 64 (halves LDS reads per MFMA), one at
+// d = 128 (register budget).
+template <int D> struct QbFor { static constexpr int value = D == 64 ? 2 : 1; };
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_t(const FwdProblem &p, hipStream_t st)
 {
-    const int n_qtiles = (p.Nq + BR - 1) / BR;
+    constexpr int QB = QbFor<D>::value;
+    using G = Geo<D, QB>;
+    const int n_qtiles = (p.Nq + G::BR - 1) / G::BR;
     const int n_bh = p.B * p.H;
     const dim3 grid((unsigned)n_qtiles * (unsigned)n_bh), block(256);
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), grid, block, 0, st,
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, QB, CAUSAL>), grid, block, 0, st,
                        static_cast<const T *>(p.q), static_cast<const T *>(p.k),
                        static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.H, p.Hkv,
                        p.Nq, p.Nk, n_bh, n_qtiles, p.scale, p.scale * kLog2e);
@@ -286,6 +498,8 @@ hipError_t launch_dt(const FwdProblem &p, hipStream_t st)
 }
 
 }  // namespace
+
+int fwd_mfma_kv_tile(int d) { return d == 64 ? Geo<64, QbFor<64>::value>::BC : Geo<128, QbFor<128>::value>::BC; }
 
 hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t st)
 {

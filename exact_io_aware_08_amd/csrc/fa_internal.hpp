@@ -40,11 +40,11 @@ struct DecodeProblem {
 };
 
 // Tile constants shared by the launchers and fa_kv_tile().
-constexpr int kFwdKvTile = 64;     // keys per KV tile, MFMA (bf16/fp16) kernel
-constexpr int kFwdQTile = 128;     // queries per workgroup (4 waves x 32)
+constexpr int kFwdQTile = 128;     // fewest queries per forward workgroup (grid-size bound)
 constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
 
-int fwd_f32_kv_tile(int d);  // keys per KV tile, fp32 / P-cast kernel
+int fwd_f32_kv_tile(int d);   // keys per KV tile, fp32 / P-cast kernel
+int fwd_mfma_kv_tile(int d);  // keys per KV tile, bf16 / fp16 kernel
 hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeProblem &p, hipStream_t stream);
