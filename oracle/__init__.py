@@ -100,10 +100,16 @@ def _load():
 
 
 def default_threads() -> int:
+    """Worker threads: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when that is set, and at 16."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return min(n, 16)
 
 
 def _f32(a) -> np.ndarray:
