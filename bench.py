@@ -143,8 +143,7 @@ def main():
             caches.append((caches[0][0].clone(), caches[0][1].clone()))
         o4 = torch.empty_like(q4)
         l4 = torch.empty((B4, H4, 1), dtype=torch.float32, device=dev)
-        ws = torch.empty(fa.decode_workspace_bytes(B4, H4, Hkv4, Nk4, d4), dtype=torch.uint8,
-                         device=dev)
+        ws = fa.decode_workspace(B4, H4, Hkv4, Nk4, d4, device=dev)
         dbytes = 2 * B4 * Hkv4 * Nk4 * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4
         us = 1e3 * _timed(lambda i: fa.decode(q4, caches[i % 4][0], caches[i % 4][1],
                                               scale=c4["scale"], workspace=ws, out=o4, lse=l4),
@@ -156,7 +155,7 @@ def main():
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": _traffic("fa_decode_gqa_bf16_pmc.md", DECODE_KERNEL),
-                            "timed": "split + merge kernels per call"}}
+                            "timed": "one launch per call (split sweep + fused merge)"}}
         if args.only == "decode":
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
                         "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})

@@ -102,24 +102,34 @@ def decode_workspace_bytes(B: int, H: int, Hkv: int, Nk: int, d: int, num_splits
     return int(load().fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits))
 
 
+def decode_workspace(B: int, H: int, Hkv: int, Nk: int, d: int, num_splits: int = 0,
+                     device="cuda"):
+    """A decode workspace (uint8 tensor) for these sizes, or None when the
+    call needs none.  Any later call it is large enough for may reuse it."""
+    need = decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+
+
 def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
            workspace=None, out=None, lse=None, return_lse: bool = True, stream=None):
-    """Split-KV decode.  q: [B,H,1,d]; k_cache, v_cache: [B,Hkv,Nk,d]."""
+    """Split-KV decode.  q: [B,H,1,d]; k_cache, v_cache: [B,Hkv,Nk,d].
+    workspace: from decode_workspace(); allocated here when not given."""
     B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k_cache, v_cache)
     if Nq != 1:
         raise ValueError("decode takes one query token per (batch, head)")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, H, Hkv, Nk, d, num_splits, q.device)
     o = out if out is not None else torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
     st = load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
                           lse.data_ptr() if lse is not None else None, B, H, Hkv, Nk, d,
-                          float(scale), _DT[q.dtype], int(num_splits), workspace.data_ptr(),
-                          workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+                          float(scale), _DT[q.dtype], int(num_splits),
+                          workspace.data_ptr() if workspace is not None else None,
+                          workspace.numel() * workspace.element_size() if workspace is not None
+                          else 0, _stream_ptr(stream))
     check(st, "fa_decode")
     return o, lse
 

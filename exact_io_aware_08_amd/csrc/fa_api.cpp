@@ -79,20 +79,42 @@ int auto_splits(int B, int H, int Hkv, int Nk)
     const int G = H / Hkv;
     const long long base = (long long)B * Hkv * ((G + 15) / 16);
     if (base <= 0 || Nk <= 0) return 1;
-    // about 1024 workgroups (4 per CU), no split shorter than 256 keys
-    long long s = (1024 + base - 1) / base;
-    const long long max_s = ((long long)Nk + 255) / 256;
+    // about one workgroup per CU (256), no split shorter than 512 keys: the
+    // sweep streams at the same rate with fewer, longer slices, and fewer
+    // splits leave less to merge
+    long long s = (256 + base - 1) / base;
+    const long long max_s = ((long long)Nk + 511) / 512;
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
     if (s > 4096) s = 4096;
     return (int)s;
 }
 
-int decode_chunk(int Nk, int splits)
+int decode_chunk(int Nk, int splits, int d)
 {
+    const long long gran = fa::decode_chunk_keys(d);
     long long ch = ((long long)Nk + splits - 1) / splits;
-    ch = ((ch + fa::kDecodeStep - 1) / fa::kDecodeStep) * fa::kDecodeStep;
-    return ch < fa::kDecodeStep ? fa::kDecodeStep : (int)ch;
+    ch = ((ch + gran - 1) / gran) * gran;
+    return ch < gran ? (int)gran : (int)ch;
+}
+
+// Decode workspace: [per-split LSE | per-split O], the second part starting
+// on a 256-byte boundary.  No workspace without a split.
+struct DecodeLayout {
+    size_t lse_off, o_off, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeLayout decode_layout(int B, int H, int Hkv, int d, int splits)
+{
+    DecodeLayout L{0, 0, 0};
+    if (splits <= 1) return L;
+    const size_t rows = (size_t)B * H * splits;
+    L.lse_off = 0;
+    L.o_off = round256(rows * sizeof(float));
+    L.total = L.o_off + rows * (size_t)d * sizeof(float);
+    return L;
 }
 
 }  // namespace
@@ -163,9 +185,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_s
 {
     const int s = fa_decode_splits(B, H, Hkv, Nk, num_splits);
     if (s < 0 || (d != 64 && d != 128)) return 0;
-    const size_t rows = (size_t)B * (size_t)H * (size_t)s;
-    const size_t o_bytes = ((rows * (size_t)d * sizeof(float)) + 255) & ~(size_t)255;
-    return o_bytes + rows * sizeof(float);
+    return decode_layout(B, H, Hkv, d, s).total;
 }
 
 fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, void *o, float *lse,
@@ -178,8 +198,8 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
     const int splits = fa_decode_splits(B, H, Hkv, Nk, num_splits);
-    const size_t need = fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits);
-    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits);
+    if (lay.total > 0 && (!workspace || workspace_bytes < lay.total)) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     const long long blocks = (long long)splits * B * Hkv * ((H / Hkv + 15) / 16);
     if (blocks > kMaxSlice) return FA_ERR_SHAPE;
@@ -189,11 +209,12 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
     p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
     p.B = B; p.H = H; p.Hkv = Hkv; p.Nk = Nk; p.d = d; p.scale = scale; p.dtype = (int)dtype;
     p.splits = splits;
-    p.chunk = decode_chunk(Nk, splits);
-    const size_t rows = (size_t)B * H * splits;
-    p.part_o = static_cast<float *>(workspace);
-    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                           (((rows * d * sizeof(float)) + 255) & ~(size_t)255));
+    p.chunk = decode_chunk(Nk, splits, d);
+    if (lay.total > 0) {
+        char *ws = static_cast<char *>(workspace);
+        p.part_lse = reinterpret_cast<float *>(ws + lay.lse_off);
+        p.part_o = reinterpret_cast<float *>(ws + lay.o_off);
+    }
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -34,9 +34,9 @@ struct DecodeProblem {
     float scale;
     int dtype;
     int splits;  // resolved (>= 1)
-    int chunk;   // keys per split, multiple of kDecodeStep
-    float *part_o;    // [B, H, splits, d]
-    float *part_lse;  // [B, H, splits]
+    int chunk;   // keys per split, multiple of decode_chunk_keys(d)
+    float *part_o;    // [B, H, splits, d]  (splits > 1)
+    float *part_lse;  // [B, H, splits]     (splits > 1)
 };
 
 // Tile constants shared by the launchers and fa_kv_tile().
@@ -45,6 +45,7 @@ constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 
 
 int fwd_f32_kv_tile(int d);   // keys per KV tile, fp32 / P-cast kernel
 int fwd_mfma_kv_tile(int d);  // keys per KV tile, bf16 / fp16 kernel
+int decode_chunk_keys(int d); // granularity of a decode split (keys)
 hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeProblem &p, hipStream_t stream);

@@ -129,11 +129,19 @@ int fa_kv_tile(fa_dtype dtype, int d, int pcast);
  *   o        : device [B, H, 1, d] (dtype);  lse: device [B, H, 1] fp32 or NULL.
  *   No mask: the new token's K/V are already in the cache.
  *   dtype    : FA_BF16 or FA_F16.
- *   num_splits: 0 = automatic (fa_decode_splits), else 1..4096.
- *   workspace: device scratch of at least
+ *   num_splits: 0 = automatic (fa_decode_splits), else 1..4096.  Splits are
+ *              whole multiples of 512 keys (d = 64) or 256 keys (d = 128);
+ *              splits past the end of the cache are empty and harmless.
+ *   workspace: device memory of at least
  *              fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits) bytes,
- *              16-byte aligned, owned by the caller; contents on entry do not
- *              matter; two calls in flight must not share it.
+ *              16-byte aligned, owned by the caller; it holds the per-split
+ *              partial results (LSE, then O on a 256-byte boundary).  Its
+ *              contents on entry do not matter.  The size is 0 when the call
+ *              has one split; workspace may then be NULL.  Calls that share a
+ *              workspace must be ordered (one stream): overlapping calls on
+ *              one workspace race.
+ *   With more than one split a second small kernel merges the partials on
+ *   the same stream; with one split the sweep writes O and LSE itself.
  */
 int fa_decode_splits(int B, int H, int Hkv, int Nk, int num_splits);
 size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits);

@@ -100,7 +100,7 @@ def test_pcast_validation(kw, expect):
 
 def _decode(ws_bytes=None, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, Hkv=2, Nk=100, d=64, scale=0.125,
-             dtype=BF16, splits=0, ws=P)
+             dtype=BF16, splits=3, ws=P)
     a.update(kw)
     need = fa.decode_workspace_bytes(a["B"], a["H"], a["Hkv"], a["Nk"], a["d"], a["splits"])
     return fa.load().fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
@@ -120,16 +120,20 @@ def test_decode_validation(kw, expect):
 
 
 def test_decode_split_policy_and_workspace():
-    # automatic split count: about 1024 workgroups, no split under 256 keys
-    assert fa.decode_splits(16, 32, 4, 8192) == 16
+    # automatic split count: about 256 workgroups, no split under 512 keys
+    assert fa.decode_splits(16, 32, 4, 8192) == 4
     assert fa.decode_splits(1, 8, 8, 100) == 1
-    assert fa.decode_splits(1, 8, 1, 1 << 20) == 1024
+    assert fa.decode_splits(1, 8, 1, 1 << 20) == 256
+    assert fa.decode_splits(1, 32, 2, 1 << 20) == 128
     assert fa.decode_splits(2, 8, 2, 100, num_splits=7) == 7
     assert fa.decode_splits(2, 8, 3, 100) == -1
+    # layout: [per-split LSE | per-split O on a 256-byte boundary]
     ws = fa.decode_workspace_bytes(16, 32, 4, 8192, 64)
-    rows = 16 * 32 * 16
-    assert ws >= rows * 64 * 4 + rows * 4
+    rows = 16 * 32 * 4
+    assert ws == rows * 4 + rows * 64 * 4
     assert fa.decode_workspace_bytes(1, 1, 1, 10, 96) == 0
+    # one split needs no workspace (the GPU tests pass none then)
+    assert fa.decode_workspace_bytes(2, 8, 2, 100, 64, 1) == 0
 
 
 def test_kv_tile_and_cast_validation():

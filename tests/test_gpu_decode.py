@@ -22,8 +22,10 @@ def run_decode(B, H, Hkv, Nk, d, dt, splits=0, seed=0, poison_ws=False):
     q, k, v = fagen.make_inputs(cfg, seed)
     ws = None
     if poison_ws:
-        nb = fa.decode_workspace_bytes(B, H, Hkv, Nk, d, splits)
-        ws = torch.full((nb // 4,), float("nan"), device="cuda").view(torch.uint8)
+        # every partial slot poisoned (NaN): each must be written before the merge
+        ws = fa.decode_workspace(B, H, Hkv, Nk, d, splits)
+        if ws is not None:
+            ws.fill_(255)
     o, lse = fa.decode(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), scale=scale,
                        num_splits=splits, workspace=ws)
     torch.cuda.synchronize()
@@ -33,7 +35,7 @@ def run_decode(B, H, Hkv, Nk, d, dt, splits=0, seed=0, poison_ws=False):
 
 def test_tinyllama_gqa_decode_bf16():
     """B=16, 32 query heads / 4 KV heads, Nk=8192, d=64, bf16 (automatic split)."""
-    assert fa.decode_splits(16, 32, 4, 8192) == 16
+    assert fa.decode_splits(16, 32, 4, 8192) == 4
     run_decode(16, 32, 4, 8192, 64, "bf16")
 
 
@@ -93,3 +95,22 @@ def test_determinism():
     o2, l2 = fa.decode(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves consecutive calls of different sizes and split
+    counts; stale partials of an earlier call never leak into a later one."""
+    need_gpu()
+    cases = [(4, 16, 2, 5000, 16), (3, 40, 2, 2100, 5), (2, 8, 8, 1300, 3), (4, 16, 2, 5000, 16)]
+    nb = max(fa.decode_workspace_bytes(B, H, Hkv, Nk, 64, s) for B, H, Hkv, Nk, s in cases)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    for i, (B, H, Hkv, Nk, s) in enumerate(cases):
+        announce(f"fa_decode reuse B={B} H={H} Hkv={Hkv} Nk={Nk} splits={s}")
+        cfg = dict(B=B, H=H, Hkv=Hkv, Nq=1, Nk=Nk, d=64, dtype="bf16", kind="iid")
+        q, k, v = fagen.make_inputs(cfg, 10 + i)
+        o, lse = fa.decode(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), scale=0.125,
+                           num_splits=s, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attention(widen(q, "bf16"), widen(k, "bf16"), widen(v, "bf16"),
+                                          False, 0.125)
+        compare(o, lse, o_ref, lse_ref, "bf16", "decode reuse")
