@@ -22,9 +22,12 @@
 //    its sum no exchange until the epilogue.
 //  * The S^T accumulator is directly the B operand of O^T = V^T P^T (after
 //    v_cvt_pk to bf16/fp16): key-slot k of lane group g in K-step t is key
-//    16t + 8(k/4) + 4g + k%4 of the 32-key block.  V^T is staged in LDS
-//    transposed ([d][key]) so the A operand is two 8-byte reads; K is staged
-//    row-major ([key][d]) and read as 16-byte A-operand rows.  Q stays in
+//    16t + 8(k/4) + 4g + k%4 of the 32-key block.  K and V are both staged
+//    row-major ([key][d]) with one 16-byte store per chunk; K is read as
+//    16-byte A-operand rows, and the V^T operand comes from two
+//    ds_read_b64_tr_b16 (within a 16-lane group, lane s gives the address of
+//    row r0 + s/4, columns c0 + 4(s%4)..+3, and lane i receives column
+//    c0 + i of rows r0..r0+3 -- four consecutive keys of one d).  Q stays in
 //    registers for the whole sweep.
 //  * Every K and V^T operand read from LDS feeds all QB query blocks of the
 //    wave, so LDS traffic per MFMA falls as QB grows (QB = 2 at d = 64,
@@ -78,16 +81,16 @@ template <int D, int QB> struct Geo {
     static constexpr int BC = 32 * NKB;          // keys per KV tile
     static constexpr int BR = NW * 32 * QB;      // queries per workgroup
     static constexpr int KSTR = D + 8;           // K tile row stride in LDS (elements)
-    static constexpr int VSTR = BC + 4;          // V^T tile row stride in LDS (elements)
+    // V tile row stride in LDS (elements): 48 dwords at d = 64, 80 at d =
+    // 128, i.e. 16 (mod 64) banks apart per row pair, so the four rows times
+    // four 8-byte column chunks that a half-wave's transpose read touches
+    // fall in distinct banks.
+    static constexpr int VS = D == 64 ? 96 : 160;
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-    static constexpr int KCH = BC * CPR / 256;   // K chunks per thread per tile
-    static constexpr int VPC = (BC / 2) * CPR;   // V (key pair, chunk) items per tile
-    static constexpr int VTH = VPC < 256 ? VPC : 256;  // threads staging V
-    static constexpr int VROUNDS = VPC / VTH;
-    static constexpr int PPR = VTH / CPR;        // key pairs per V round
+    static constexpr int KCH = BC * CPR / 256;   // K (and V) chunks per thread per tile
     static_assert(QB * NKB == 2, "two 32x32 score blocks per wave");
-    static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "K staging split");
-    static_assert(VTH % 64 == 0 && VROUNDS * VTH == VPC && PPR % 16 == 0, "V staging split");
+    static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "staging split");
+    static_assert(VS >= D && (VS * 2) % 16 == 0, "V row stride");
 };
 
 // Buffer resource over rows [j0, rows) of a row-major slice of D-element
@@ -100,86 +103,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int r
                                              kBufferFlags);
 }
 
-// Per-thread offsets of the staging loads and LDS stores within a tile.
-//  K: chunk ci = tid + 256 r -> row ci / CPR, chunk ci % CPR (row-major,
-//     coalesced).
-//  V: threads tid < VTH; lane l of 32-lane group g handles key pair kp and
-//     chunk cc with kp = l % 16 + PPR r and cc = l / 16 + 2 g, so the 32
-//     dwords a half-wave writes into V^T land in 32 distinct banks.
+// Per-thread offsets of the staging loads and LDS stores within a tile:
+// chunk ci = tid + 256 r -> row ci / CPR, chunk ci % CPR (row-major,
+// coalesced).  K and V use the same map, with their own LDS row strides.
 template <int D, int QB> struct KvMap {
     using G = Geo<D, QB>;
-    int koff[G::KCH];      // byte offsets of the K chunks
-    int kst[G::KCH];       // LDS element offsets of the K chunks
-    int voff[G::VROUNDS];  // byte offset of key 2kp, chunk cc (key 2kp+1 is + D elements)
-    int vst[G::VROUNDS];   // LDS element offset of V^T[8cc][2kp]
+    int off[G::KCH];  // byte offsets of the chunks in global memory
+    int kst[G::KCH];  // LDS element offsets in the K tile
+    int vst[G::KCH];  // LDS element offsets in the V tile
     __device__ __forceinline__ KvMap(int tid, int elem_bytes) {
 #pragma unroll
         for (int r = 0; r < G::KCH; ++r) {
             const int ci = tid + r * 256;
-            koff[r] = ((ci / G::CPR) * D + (ci % G::CPR) * 8) * elem_bytes;
+            off[r] = ((ci / G::CPR) * D + (ci % G::CPR) * 8) * elem_bytes;
             kst[r] = (ci / G::CPR) * G::KSTR + (ci % G::CPR) * 8;
-        }
-        const int l = tid & 31, g = (tid >> 5) & (G::VTH / 32 - 1);
-#pragma unroll
-        for (int r = 0; r < G::VROUNDS; ++r) {
-            const int kp = (l & 15) + G::PPR * r;
-            const int cc = (l >> 4) + 2 * g;
-            voff[r] = ((2 * kp) * D + cc * 8) * elem_bytes;
-            vst[r] = (cc * 8) * G::VSTR + 2 * kp;
+            vst[r] = (ci / G::CPR) * G::VS + (ci % G::CPR) * 8;
         }
     }
 };
 
 template <typename T, int D, int QB>
-__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rs, const KvMap<D, QB> &mp,
-                                       u32x4_t (&kreg)[Geo<D, QB>::KCH])
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, const KvMap<D, QB> &mp,
+                                          u32x4_t (&reg)[Geo<D, QB>::KCH])
 {
 #pragma unroll
     for (int r = 0; r < Geo<D, QB>::KCH; ++r)
-        kreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.koff[r], 0, 0);
+        reg[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.off[r], 0, 0);
 }
 
+// Registers -> LDS, row-major [key][d] (K and V alike; V is read back
+// transposed by ds_read_b64_tr_b16).
 template <typename T, int D, int QB>
-__device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rs, const KvMap<D, QB> &mp,
-                                       u32x4_t (&vreg)[2 * Geo<D, QB>::VROUNDS])
+__device__ __forceinline__ void store_rows(T *buf, const int (&st)[Geo<D, QB>::KCH],
+                                           const u32x4_t (&reg)[Geo<D, QB>::KCH])
 {
 #pragma unroll
-    for (int r = 0; r < Geo<D, QB>::VROUNDS; ++r) {
-        vreg[2 * r] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.voff[r], 0, 0);
-        vreg[2 * r + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, mp.voff[r] + D * (int)sizeof(T), 0, 0);
-    }
+    for (int r = 0; r < Geo<D, QB>::KCH; ++r) *reinterpret_cast<u32x4_t *>(&buf[st[r]]) = reg[r];
 }
 
-// Registers -> LDS: K row-major [key][d].
-template <typename T, int D, int QB>
-__device__ __forceinline__ void store_k(T *Ks, const KvMap<D, QB> &mp,
-                                        const u32x4_t (&kreg)[Geo<D, QB>::KCH])
-{
-#pragma unroll
-    for (int r = 0; r < Geo<D, QB>::KCH; ++r) *reinterpret_cast<u32x4_t *>(&Ks[mp.kst[r]]) = kreg[r];
-}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// Registers -> LDS: V transposed [d][key], keys 2kp (low half) and 2kp+1
-// (high half) packed per dword.
-template <typename T, int D, int QB>
-__device__ __forceinline__ void store_v(T *Vt, const KvMap<D, QB> &mp,
-                                        const u32x4_t (&vreg)[2 * Geo<D, QB>::VROUNDS])
+// Four 16-bit values of one column from four consecutive rows (see the
+// transpose-read layout in the kernel comment).
+template <typename T>
+__device__ __forceinline__ u32x2_t read_tr(const T *p)
 {
-    using G = Geo<D, QB>;
-#pragma unroll
-    for (int r = 0; r < G::VROUNDS; ++r) {
-        const u32x4_t a = vreg[2 * r], bq = vreg[2 * r + 1];
-        uint32_t *base = reinterpret_cast<uint32_t *>(&Vt[mp.vst[r]]);
-        constexpr int RS = G::VSTR / 2;  // V^T row stride in dwords
-        base[0 * RS] = pack_lo16(a.x, bq.x);
-        base[1 * RS] = pack_hi16(a.x, bq.x);
-        base[2 * RS] = pack_lo16(a.y, bq.y);
-        base[3 * RS] = pack_hi16(a.y, bq.y);
-        base[4 * RS] = pack_lo16(a.z, bq.z);
-        base[5 * RS] = pack_hi16(a.z, bq.z);
-        base[6 * RS] = pack_lo16(a.w, bq.w);
-        base[7 * RS] = pack_hi16(a.w, bq.w);
-    }
+    return bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p)));
 }
 
 // S^T blocks (32 keys x 32 queries each) = K_tile Q_wave^T; block index
@@ -226,10 +196,10 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     using v8 = typename M::v8;
     using P2 = Pack2<T>;
     using G = Geo<D, QB>;
-    constexpr int BC = G::BC, NKB = G::NKB, VSTR = G::VSTR;
+    constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS;
 
     __shared__ __attribute__((aligned(16))) T Kbuf[2][BC * G::KSTR];
-    __shared__ __attribute__((aligned(16))) T Vbuf[2][D * VSTR];
+    __shared__ __attribute__((aligned(16))) T Vbuf[2][BC * VS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
@@ -283,22 +253,25 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     }
 
     const KvMap<D, QB> mp(tid, (int)sizeof(T));
-    const bool stages_v = tid < G::VTH;  // wave-uniform
-    u32x4_t kreg[G::KCH], vreg[2 * G::VROUNDS];
+    // Transpose-read address of this lane within a V tile: 16-lane group
+    // (hh, c / 16) reads rows 4hh + (lane % 16) / 4 (+ the K-step's first
+    // key) and columns 16 (c / 16) + 4 (lane % 16 % 4) (+ 32 mb).
+    const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VS + 16 * (c >> 4) + 4 * (lane & 3);
+    u32x4_t kreg[G::KCH], vreg[G::KCH];
     f32x16_t s_a[2], s_b[2];
     auto tile = [&](int jj) { return min(jj, nkt - 1) * BC; };  // clamped first key of a tile
 
     if (nkt > 0) {
         // prologue: K0 -> Kbuf[0], V0 -> Vbuf[0], K1 -> Kbuf[1]; registers
         // then hold K2 and V1.
-        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, 0), mp, kreg);
-        if (stages_v) load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, 0), mp, vreg);
-        store_k<T, D, QB>(Kbuf[0], mp, kreg);
-        if (stages_v) store_v<T, D, QB>(Vbuf[0], mp, vreg);
-        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(1)), mp, kreg);
-        if (stages_v) load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(1)), mp, vreg);
-        store_k<T, D, QB>(Kbuf[1], mp, kreg);
-        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(2)), mp, kreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, 0), mp, kreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, 0), mp, vreg);
+        store_rows<T, D, QB>(Kbuf[0], mp.kst, kreg);
+        store_rows<T, D, QB>(Vbuf[0], mp.vst, vreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(1)), mp, kreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(1)), mp, vreg);
+        store_rows<T, D, QB>(Kbuf[1], mp.kst, kreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(2)), mp, kreg);
         lds_barrier();
         scores<T, D, QB>(Kbuf[0], qop, c, hh, s_a);
         lds_barrier();  // Kbuf[0] is overwritten in iteration 0
@@ -307,9 +280,8 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // One KV tile.  Invariant on entry: sc = S^T of tile j; Kbuf[(j+1)&1] =
     // K_{j+1}; Vbuf[j&1] = V_j; kreg = K_{j+2}; vreg = V_{j+1} (tile indices
     // past the last tile are clamped to it; those copies go to buffers that
-    // are never read again).  The staging is branch-free apart from the
-    // wave-uniform choice of which waves stage V, so the only waits on
-    // global loads are for data requested a full tile earlier.  Tiles past
+    // are never read again).  The staging is branch-free, so the only waits
+    // on global loads are for data requested a full tile earlier.  Tiles past
     // a wave's causal limit are processed fully masked (weight 0), which
     // keeps the hot blocks free of branches so the scheduler can interleave
     // MFMA and VALU instructions within the wave.
@@ -415,27 +387,27 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 
         // ---- hot block 2: O^T += V_j^T P^T, interleaved with staging the
         //      next tiles into the LDS buffers not read in this step ----
-        const T *Vt = Vbuf[j & 1];
+        const T *Vs = Vbuf[j & 1] + tr_off;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const T *vp = &Vt[(32 * mb + c) * VSTR + kb * 32 + 16 * t + 4 * hh];
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vp);
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vp + 8);
+                    // K-slots 0-3: keys 16t + 4hh + 0..3, slots 4-7: 16t + 8 + 4hh + 0..3
+                    // (of block kb), column d = 32 mb + c: the S^T register order.
+                    const T *vp = Vs + (kb * 32 + 16 * t) * VS + 32 * mb;
+                    const u32x2_t lo = read_tr(vp);
+                    const u32x2_t hi = read_tr(vp + 8 * VS);
                     const v8 vop = bitcast<v8>(u32x4_t{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
                         acc[qb][mb] = M::mma32(vop, pop[qb * NKB + kb][t], acc[qb][mb]);
                 }
-        store_k<T, D, QB>(Kbuf[j & 1], mp, kreg);
-        load_k<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(j + 3)), mp, kreg);
-        if (stages_v) {
-            store_v<T, D, QB>(Vbuf[(j + 1) & 1], mp, vreg);
-            load_v<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(j + 2)), mp, vreg);
-        }
+        store_rows<T, D, QB>(Kbuf[j & 1], mp.kst, kreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(j + 3)), mp, kreg);
+        store_rows<T, D, QB>(Vbuf[(j + 1) & 1], mp.vst, vreg);
+        load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(j + 2)), mp, vreg);
         lds_barrier();
     };
 
