@@ -75,7 +75,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="oracle rows per head for the CPU leg (0: every row, about 10 s on 16 cores)")
@@ -147,7 +147,7 @@ def main():
         dbytes = 2 * B4 * Hkv4 * Nk4 * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4
         us = 1e3 * _timed(lambda i: fa.decode(q4, caches[i % 4][0], caches[i % 4][1],
                                               scale=c4["scale"], workspace=ws, out=o4, lse=l4),
-                          args.decode_steps, 50, torch)
+                          args.decode_steps, 400, torch)
         gbs = dbytes / (us * 1e-6) / 1e9
         dec = {"workload": "gqa_decode_bf16", "B": B4, "H": H4, "Hkv": Hkv4, "Nk": Nk4, "d": d4,
                "splits": fa.decode_splits(B4, H4, Hkv4, Nk4), "value": round(gbs, 1),
@@ -155,7 +155,7 @@ def main():
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": _traffic("fa_decode_gqa_bf16_pmc.md", DECODE_KERNEL),
-                            "timed": "one launch per call (split sweep + fused merge)"}}
+                            "timed": "sweep + merge kernels per call"}}
         if args.only == "decode":
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
                         "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})

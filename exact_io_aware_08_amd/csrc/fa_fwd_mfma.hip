@@ -199,7 +199,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS;
 
     __shared__ __attribute__((aligned(16))) T Kbuf[2][BC * G::KSTR];
-    __shared__ __attribute__((aligned(16))) T Vbuf[2][BC * VS];
+    __shared__ __attribute__((aligned(16))) T Vbuf[3][BC * VS];  // tile i in Vbuf[i % 3]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
@@ -259,13 +259,21 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VS + 16 * (c >> 4) + 4 * (lane & 3);
     u32x4_t kreg[G::KCH], vreg[G::KCH];
     f32x16_t s_a[2], s_b[2];
+    v8 p_a[2][2], p_b[2][2];  // P^T operands [score block][K-step] of two consecutive tiles
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) p_a[sb][t] = bitcast<v8>(u32x4_t{0u, 0u, 0u, 0u});
     auto tile = [&](int jj) { return min(jj, nkt - 1) * BC; };  // clamped first key of a tile
 
     if (nkt > 0) {
         // prologue: K0 -> Kbuf[0], V0 -> Vbuf[0], K1 -> Kbuf[1]; registers
-        // then hold K2 and V1.
+        // then hold K2 and V1.  Vbuf[2] stands for tile -1, whose (zero) P
+        // is multiplied in the first step: it must hold finite values.
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, 0), mp, kreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, 0), mp, vreg);
+        for (int i = tid; i < BC * VS / 8; i += 256)
+            reinterpret_cast<u32x4_t *>(Vbuf[2])[i] = u32x4_t{0u, 0u, 0u, 0u};
         store_rows<T, D, QB>(Kbuf[0], mp.kst, kreg);
         store_rows<T, D, QB>(Vbuf[0], mp.vst, vreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(1)), mp, kreg);
@@ -277,15 +285,40 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         lds_barrier();  // Kbuf[0] is overwritten in iteration 0
     }
 
-    // One KV tile.  Invariant on entry: sc = S^T of tile j; Kbuf[(j+1)&1] =
-    // K_{j+1}; Vbuf[j&1] = V_j; kreg = K_{j+2}; vreg = V_{j+1} (tile indices
-    // past the last tile are clamped to it; those copies go to buffers that
-    // are never read again).  The staging is branch-free, so the only waits
-    // on global loads are for data requested a full tile earlier.  Tiles past
-    // a wave's causal limit are processed fully masked (weight 0), which
-    // keeps the hot blocks free of branches so the scheduler can interleave
-    // MFMA and VALU instructions within the wave.
-    auto step = [&](int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    // O^T += V^T P^T for one tile whose V is in Vs (transpose reads).
+    auto pv = [&](const T *Vs, const v8 (&pp)[2][2]) {
+        Vs += tr_off;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    // K-slots 0-3: keys 16t + 4hh + 0..3, slots 4-7: 16t + 8 + 4hh + 0..3
+                    // (of block kb), column d = 32 mb + c: the S^T register order.
+                    const T *vp = Vs + (kb * 32 + 16 * t) * VS + 32 * mb;
+                    const u32x2_t lo = read_tr(vp);
+                    const u32x2_t hi = read_tr(vp + 8 * VS);
+                    const v8 vop = bitcast<v8>(u32x4_t{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        acc[qb][mb] = M::mma32(vop, pp[qb * NKB + kb][t], acc[qb][mb]);
+                }
+    };
+
+    // One KV tile.  Invariant on entry: sc = S^T of tile j; pp = P of tile
+    // j-1 (zero for j = 0); Kbuf[(j+1)&1] = K_{j+1}; Vbuf[(j-1)%3] = V_{j-1},
+    // Vbuf[j%3] = V_j; kreg = K_{j+2}; vreg = V_{j+1} (tile indices past the
+    // last tile are clamped to it; those copies go to buffers that are never
+    // read again).  The product with V of tile j is deferred to step j+1, so
+    // every step interleaves 16 MFMAs (S^T of tile j+1 and P V of tile j-1)
+    // with the softmax of tile j on the VALU.  The staging is branch-free,
+    // so the only waits on global loads are for data requested a full tile
+    // earlier.  Tiles past a wave's causal limit are processed fully masked
+    // (weight 0), which keeps the hot block free of branches.
+    auto step = [&](int j, int vb, f32x16_t (&sc)[2], f32x16_t (&sn)[2], const v8 (&pp)[2][2],
+                    v8 (&pc)[2][2]) {
+        const int vprev = vb == 0 ? 2 : vb - 1, vnext = vb == 2 ? 0 : vb + 1;
         const int j0 = j * BC;
         // ---- mask: ragged last tile, the diagonal band and beyond (causal) ----
         const bool need_mask = (j0 + BC > Nk) || (CAUSAL && j0 + BC - 1 > q0w + off);
@@ -304,22 +337,38 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         }
 
         // ---- reference max ----
-        // Set from the exact row max on the first tile (and for rows that
-        // have not seen a key yet).  Afterwards it is only moved when a
-        // tile's exponentials leave the safe range, which the row sums below
+        // A row takes the exact max of its first tile with a visible key as
+        // its reference.  Afterwards the reference only moves when a tile's
+        // exponentials leave the safe range, which the row sums below
         // detect; the per-tile row max is then never computed on the common
         // path.  Any finite reference gives the same O and LSE.
+        auto tile_max = [&](int qb) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb * NKB + kb][r]);
+            return max_pair(m);
+        };
+        // Rows without a reference yet have no weight in acc or l, so setting
+        // theirs needs no rescale (and commutes with the deferred P V).
+        bool fresh = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) fresh |= (m_ref[qb] == -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(fresh) != 0) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m = tile_max(qb);
+                m_ref[qb] = m_ref[qb] == -INFINITY ? m : m_ref[qb];
+            }
+        }
+        // Any row: raise the reference to this tile's max, rescaling what
+        // acc and l hold (everything up to tile j-1 -- the P V of tile j-1
+        // is already in acc when this runs).
         auto rebase = [&]() {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float m = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[qb * NKB + kb][r]);
-                m = max_pair(m);
-                // alpha = 1 on rows that keep their reference (including rows
-                // still without any visible key); 0 when the old one was -inf.
+                const float m = tile_max(qb);
                 const bool raise = m > m_ref[qb];
                 const float alpha = raise ? fast_exp2((m_ref[qb] - m) * scale_log2) : 1.f;
                 m_ref[qb] = raise ? m : m_ref[qb];
@@ -328,13 +377,8 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                 for (int i = 0; i < D / 32; ++i) acc[qb][i] *= alpha;
             }
         };
-        bool fresh = (j == 0);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) fresh |= (m_ref[qb] == -INFINITY);
-        if (__builtin_amdgcn_ballot_w64(fresh) != 0) rebase();
 
         // P = exp2(s*c - m*c) packed to 16-bit, with this tile's row sums.
-        v8 pop[2][2];  // [score block][K-step]
         float ts[QB];
         auto make_p = [&]() {
             float mneg[QB];
@@ -354,23 +398,28 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                         const float p0 = fast_exp2(fmaf(sc[sb][8 * t + 2 * e], scale_log2, mneg[qb]));
                         const float p1 = fast_exp2(fmaf(sc[sb][8 * t + 2 * e + 1], scale_log2, mneg[qb]));
                         pk[e] = __builtin_convertvector((f32x2_t{p0, p1}), typename P2::v2);
+                        // keep each conversion here: without this the compiler
+                        // sinks all of them past the range-check branch below,
+                        // out of the MFMA-interleaved block
+                        asm volatile("" : "+v"(pk[e]));
                         ts[qb] = P2::add(pk[e], p0, p1, ts[qb]);
                     }
-                    pop[sb][t] = bitcast<v8>(u32x4_t{bitcast<uint32_t>(pk[0]), bitcast<uint32_t>(pk[1]),
-                                                     bitcast<uint32_t>(pk[2]), bitcast<uint32_t>(pk[3])});
+                    pc[sb][t] = bitcast<v8>(u32x4_t{bitcast<uint32_t>(pk[0]), bitcast<uint32_t>(pk[1]),
+                                                    bitcast<uint32_t>(pk[2]), bitcast<uint32_t>(pk[3])});
                 }
         };
 
-        // ---- hot block 1: S^T of tile j+1 on the MFMA pipe while the VALU
-        //      turns tile j into P (exp2, cvt to 16-bit, row sums) ----
+        // ---- hot block: S^T of tile j+1 and P V of tile j-1 on the MFMA
+        //      pipe while the VALU turns tile j into P ----
         scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, sn);
+        pv(Vbuf[vprev], pp);
         make_p();
-        constexpr int N_S_MFMA = 2 * (D / 16);
-        __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (D / 16), 0);  // K operand LDS reads
+        constexpr int N_MFMA = 2 * (D / 16) + 2 * (D / 32) * 2;
+        __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (D / 16) + 2 * (D / 32) * NKB * 2, 0);  // LDS reads
 #pragma unroll
-        for (int i = 0; i < N_S_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x0002, 96 / N_S_MFMA, 0);   // VALU
+        for (int i = 0; i < N_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);             // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x0002, 112 / N_MFMA, 0);  // VALU
         }
 
         // Range check: exponentials above 2^64 per tile (or inf/NaN) mean the
@@ -385,36 +434,30 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] += ts[qb];
 
-        // ---- hot block 2: O^T += V_j^T P^T, interleaved with staging the
-        //      next tiles into the LDS buffers not read in this step ----
-        const T *Vs = Vbuf[j & 1] + tr_off;
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    // K-slots 0-3: keys 16t + 4hh + 0..3, slots 4-7: 16t + 8 + 4hh + 0..3
-                    // (of block kb), column d = 32 mb + c: the S^T register order.
-                    const T *vp = Vs + (kb * 32 + 16 * t) * VS + 32 * mb;
-                    const u32x2_t lo = read_tr(vp);
-                    const u32x2_t hi = read_tr(vp + 8 * VS);
-                    const v8 vop = bitcast<v8>(u32x4_t{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        acc[qb][mb] = M::mma32(vop, pop[qb * NKB + kb][t], acc[qb][mb]);
-                }
+        // ---- staging of the next tiles into buffers not read in this step ----
         store_rows<T, D, QB>(Kbuf[j & 1], mp.kst, kreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(j + 3)), mp, kreg);
-        store_rows<T, D, QB>(Vbuf[(j + 1) & 1], mp.vst, vreg);
+        store_rows<T, D, QB>(Vbuf[vnext], mp.vst, vreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(j + 2)), mp, vreg);
         lds_barrier();
     };
 
-    // Unrolled by two so the score registers swap roles instead of being copied.
+    // Unrolled by two so the score and P registers swap roles instead of
+    // being copied.
+    int vb = 0;  // j % 3
     for (int j = 0; j < nkt; j += 2) {
-        step(j, s_a, s_b);
-        if (j + 1 < nkt) step(j + 1, s_b, s_a);
+        step(j, vb, s_a, s_b, p_a, p_b);
+        vb = vb == 2 ? 0 : vb + 1;
+        if (j + 1 < nkt) {
+            step(j + 1, vb, s_b, s_a, p_b, p_a);
+            vb = vb == 2 ? 0 : vb + 1;
+        }
+    }
+    // the deferred P V of the last tile (V of tile nkt-1 is in Vbuf[(nkt-1)%3])
+    if (nkt > 0) {
+        const int vlast = vb == 0 ? 2 : vb - 1;
+        if (nkt & 1) pv(Vbuf[vlast], p_b);
+        else pv(Vbuf[vlast], p_a);
     }
 
     // ---- epilogue: O = acc / l, LSE = m*scale + ln l ----
