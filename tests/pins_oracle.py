@@ -30,6 +30,7 @@ FP8"; [FV] gist.science "FlashAttention for Scalable Vector Architectures".
 from __future__ import annotations
 
 import math
+import os
 
 import mpmath
 import numpy as np
@@ -38,6 +39,22 @@ import torch
 import oracle
 
 RNG = np.random.default_rng(1234)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(fname: str) -> dict:
+    """name -> float from a cited fixture in tests/golden (2^k allowed)."""
+    out = {}
+    for line in open(os.path.join(GOLDEN, fname)):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        name, rest = line.split("=", 1)
+        val = rest.split("|", 1)[0].strip()
+        out[name.strip()] = 2.0 ** float(val[2:]) if val.startswith("2^") else float(val)
+    return out
 
 
 def _rand(*shape, scale=1.0):
@@ -328,16 +345,20 @@ def pin_row_subset_and_threads():
 def pin_e4m3_page_constants():
     """[PC]: 3-bit mantissa; round-to-zero threshold 2^-10 ("Marco Teorico");
     normal range from 2^-6, largest value 448 ("Optimizacion 2")."""
+    g = golden("pcast_page_values.txt")
     dec = oracle.e4m3_decode(np.arange(256))
-    assert dec[0x01] == 2.0 ** -9 and dec[0x08] == 2.0 ** -6 and dec[0x7E] == 448.0
-    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
     fin = dec[np.isfinite(dec)]
-    assert fin.max() == 448.0 and np.min(fin[fin > 0]) == 2.0 ** -9
-    t = np.float32(2.0 ** -10)
-    assert oracle.e4m3_encode(t) == 0                                  # tie -> even (0)
-    assert oracle.e4m3_encode(np.nextafter(t, np.float32(1))) == 1     # just above -> 2^-9
-    # one mantissa step between 1 and 2 is 2^-3 (3-bit mantissa)
-    assert dec[0x39] - dec[0x38] == 0.125 and dec[0x38] == 1.0
+    assert fin.max() == g["max_finite"] and dec[0x7E] == g["max_finite"]
+    assert np.min(fin[fin >= g["min_normal"]]) == g["min_normal"] == dec[0x08]
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    # everything at or below the round-to-zero threshold encodes to 0 (the
+    # tie goes to the even code 0), anything above it to a nonzero code
+    t = np.float32(g["round_to_zero"])
+    assert oracle.e4m3_encode(t) == 0
+    assert oracle.e4m3_encode(np.nextafter(t, np.float32(1))) != 0
+    assert np.min(fin[fin > 0]) == 2 * g["round_to_zero"]  # smallest subnormal
+    # mantissa bits: one step between 1 and 2 is 2^-(bits)
+    assert dec[0x39] - dec[0x38] == 2.0 ** -g["e4m3_mantissa_bits"] and dec[0x38] == 1.0
 
 
 def pin_e4m3_vs_torch():
@@ -370,20 +391,23 @@ def pin_expected_max_gauss():
     d4 = oracle.expected_max_gauss(4)
     mc = np.random.default_rng(5).standard_normal((2_000_000, 4)).max(axis=1).mean()
     assert abs(d4 - mc) < 3e-3
-    assert abs(d4 - 1.0) < 0.05   # [PC] "Marco Teorico": roughly 1.0 for k = 4
+    # [PC] "Marco Teorico" prints "roughly 1.0" for k = 4 (exact value 1.0294)
+    assert abs(d4 - golden("pcast_page_values.txt")["delta_k4"]) < 0.05
 
 
 def pin_F_closed_form():
+    g = golden("pcast_page_values.txt")
     d4 = oracle.expected_max_gauss(4)
-    # 6.93 is 10 ln 2, the log of the 2^-10 round-to-zero threshold
-    assert abs(10 * math.log(2) - 6.93) < 5e-3
+    # 6.93 is -ln of the 2^-10 round-to-zero threshold
+    assert abs(-math.log(g["round_to_zero"]) - g["ln_round_to_zero"]) < 5e-3
     for S in (1.0, 256.0, 448.0):
         dc = oracle.delta_c(S, d4)
-        assert abs(dc - (6.93 + math.log(S) - d4)) < 5e-3          # "Contribuciones Clave"
+        assert abs(dc - (g["ln_round_to_zero"] + math.log(S) - d4)) < 5e-3  # "Contribuciones Clave"
         assert abs(oracle.F_closed_form(dc, S, d4) - 0.5) < 1e-12
     # threshold effect near Delta 6-7 for S = 1 ("Marco Teorico")
-    assert oracle.F_closed_form(4, 1, d4) < 0.05 < 0.5 < oracle.F_closed_form(7, 1, d4)
-    assert 6.0 - 0.2 < oracle.delta_c(1.0, d4) < 7.0
+    lo, hi = g["collapse_delta_lo"], g["collapse_delta_hi"]
+    assert oracle.F_closed_form(lo - 2, 1, d4) < 0.05 < 0.5 < oracle.F_closed_form(hi, 1, d4)
+    assert lo - 0.2 < oracle.delta_c(1.0, d4) < hi
     # monotone in Delta, decreasing in S
     fs = [oracle.F_closed_form(x, 1, d4) for x in np.linspace(0, 14, 29)]
     assert all(a < b for a, b in zip(fs, fs[1:]))
@@ -397,22 +421,36 @@ def pin_F_closed_form():
         assert abs(frac - oracle.F_closed_form(delta, S, d4)) < 2e-3
     # "Optimizacion 1": reverse order, S = 256, N <= 1e6: the pre-sink max is a
     # max of N standard normals, and the flush probability stays below 1e-12
+    n_max = g["reverse256_max_n"]
     m_pre = 4.9  # E[max of 1e6 N(0,1)] is about 4.86
-    assert oracle.Phi(m_pre - 10 * math.log(2) - math.log(256.0)) < 1e-12
+    assert n_max == 1e6
+    assert oracle.Phi(m_pre - g["ln_round_to_zero"] - math.log(256.0)) < g["reverse256_bound"]
 
 
 def pin_dp():
     """[PC] "Optimizacion 2": d_p(S) is a sawtooth whose lower envelope is at
     powers of two with value 2^-4; S = 448 sits 14% above it; 2^-6/256 = 2^-14."""
+    g = golden("pcast_page_values.txt")
     for kexp in range(0, 9):
-        assert oracle.dp(2.0 ** kexp) == 2.0 ** -4
-    assert abs(oracle.dp(448.0) / 2.0 ** -4 - 1.14) < 0.01
+        assert oracle.dp(2.0 ** kexp) == g["dp_envelope"]
+    assert abs(oracle.dp(448.0) / g["dp_envelope"] - (1 + g["dp_448_excess"])) < 0.01
     # brute force over the code table for representable S: (S - pred(S)) / S
     dec = oracle.e4m3_decode(np.arange(0x7F)).astype(np.float64)
     for S in (1.0, 2.0, 16.0, 240.0, 256.0, 320.0, 416.0, 448.0):
         pred = dec[dec < S].max()
         assert abs(oracle.dp(S) - (S - pred) / S) < 1e-15, S
-    assert 2.0 ** -6 / 256 == 2.0 ** -14
+    assert g["min_normal"] / 256 == g["coverage_256"]
+
+
+def pin_trading_day_workload():
+    """[MM] opening paragraphs: a day of 23,400 one-second steps, 12 heads,
+    an fp16 score matrix of about 12.9 GB -- the full-size prefill shape."""
+    import fagen
+    g = golden("trading_day.txt")
+    c3 = fagen.CONFIGS[3]
+    assert c3["Nq"] == c3["Nk"] == g["steps_per_day"] == 6.5 * 3600 and c3["H"] == g["heads"]
+    gb = g["steps_per_day"] ** 2 * g["heads"] * 2 / 1e9
+    assert abs(gb - g["score_matrix_gb_printed"]) / g["score_matrix_gb_printed"] < 0.10
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
