@@ -81,6 +81,8 @@ def main():
                     help="oracle rows per head for the CPU leg (0: every row, about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (tiny fp32, GPT-2-small prefill, P-cast sink)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -161,6 +163,55 @@ def main():
                         "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})
         out["decode"] = dec
 
+    # ---------------- the other workloads (reported, not the step) ----------------
+    if args.only == "all" and not args.no_extra:
+        extra = {}
+        # tiny exact fp32 check (launch-bound)
+        c1 = fagen.CONFIGS[1]
+        q1n, k1n, v1n = fagen.make_inputs(c1, 0)
+        q1, k1, v1 = (to_dev(x, "f32") for x in (q1n, k1n, v1n))
+        ms1 = _timed(lambda i: fa.fwd(q1, k1, v1, causal=False, scale=c1["scale"]), 200, 50, torch)
+        extra["tiny_exact_f32"] = {"us_per_call": round(ms1 * 1e3, 2), "shape": [1, 1, 256, 64],
+                                   "causal": False}
+        # GPT-2-small-shaped prefill
+        c2 = fagen.CONFIGS[2]
+        q2n, k2n, v2n = fagen.make_inputs(c2, 0)
+        q2, k2, v2 = (to_dev(x, "bf16") for x in (q2n, k2n, v2n))
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty(q2.shape[:3], dtype=torch.float32, device=dev)
+        ms2 = _timed(lambda i: fa.fwd(q2, k2, v2, causal=True, scale=c2["scale"], out=o2, lse=l2),
+                     50, 50, torch)
+        f2 = 2.0 * 64 * 4 * 12 * 2048 * 2049
+        extra["gpt2s_prefill_bf16"] = {"ms_per_call": round(ms2, 4),
+                                       "tflops": round(f2 / (ms2 * 1e-3) / 1e12, 1),
+                                       "frac_of_bf16_peak": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                       "shape": [4, 12, 2048, 64], "causal": True}
+        # P-cast on the attention-sink workload: flush counters and time per run
+        c5 = fagen.CONFIGS[5]
+        B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
+        q5n, k5n, v5n = fagen.sink_inputs(0, B5, H5, N5, d5, 0.0)
+        q5, v5 = to_dev(q5n, "f32"), to_dev(v5n, "f32")
+        k5_base = to_dev(k5n, "f32")
+        pc = {}
+        for delta in c5["deltas"]:
+            k5 = k5_base.clone()
+            k5[:, :, :4, 0] += float(np.float32(delta * math.sqrt(d5)))
+            for name, (S, rev) in (("fwd_S1", (1.0, False)), ("rev_S256", (256.0, True))):
+                res = {}
+                ms5 = _timed(lambda i: fa.fwd_pcast(q5, k5, v5, causal=True, scale=c5["scale"],
+                                                    p_scale=S, kv_reverse=rev, n_sink=4),
+                             3, 1, torch)
+                o5, _, cnt = fa.fwd_pcast(q5, k5, v5, causal=True, scale=c5["scale"], p_scale=S,
+                                          kv_reverse=rev, n_sink=4)
+                cnt = [int(x) for x in cnt.cpu()]
+                res.update({"ms_per_call": round(ms5, 3), "casts": cnt[0], "flushed": cnt[1],
+                            "flush_frac": cnt[1] / max(cnt[0], 1),
+                            "flushed_outside_sink_tiles": cnt[3]})
+                pc[f"delta{delta:g}_{name}"] = res
+            del k5
+        extra["pcast_sink_f32"] = {"shape": [B5, H5, N5, d5], "runs": pc}
+        out["other_workloads"] = extra
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -197,6 +248,30 @@ def main():
                                          f"N={N} causal prefill ({pairs:.3g} visible pairs, "
                                          f"{cpu_s:.1f} s wall); fp64 correctness oracle, not an "
                                          f"optimised CPU baseline"}
+    if "other_workloads" in out and not args.no_cpu_baseline:
+        # the P-cast report against the oracle: closed-form flush fraction
+        # F(Delta, S) and MSE against exact attention on sampled rows
+        import oracle
+        d4 = oracle.expected_max_gauss(4)
+        c5 = fagen.CONFIGS[5]
+        B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
+        rows5 = np.stack([fagen.sample_rows(1, h, N5, 8) for h in range(H5)])
+        q5n, k5n, v5n = fagen.sink_inputs(0, B5, H5, N5, d5, 0.0)
+        for delta in c5["deltas"]:
+            k5n_d = k5n.copy()
+            k5n_d[:, :, :4, 0] += np.float32(delta * math.sqrt(d5))
+            o_ex, _ = oracle.attention(q5n, k5n_d, v5n, True, c5["scale"], rows=rows5,
+                                       nthreads=oracle.default_threads())
+            k5d = to_dev(k5n_d, "f32")
+            q5d, v5d = to_dev(q5n, "f32"), to_dev(v5n, "f32")
+            for name, (S, rev) in (("fwd_S1", (1.0, False)), ("rev_S256", (256.0, True))):
+                o5, _, _ = fa.fwd_pcast(q5d, k5d, v5d, causal=True, scale=c5["scale"], p_scale=S,
+                                        kv_reverse=rev, n_sink=4)
+                og = o5.cpu().numpy()[0][np.arange(H5)[:, None], rows5]
+                r = out["other_workloads"]["pcast_sink_f32"]["runs"][f"delta{delta:g}_{name}"]
+                r["mse_vs_exact_sampled"] = float(np.mean((og - o_ex[0]) ** 2))
+                r["F_closed_form"] = float(oracle.F_closed_form(delta, S, d4))
+        out["other_workloads"]["pcast_sink_f32"]["mse_rows"] = "8 seeded rows per head"
     print(json.dumps(out))
 
 
