@@ -170,7 +170,7 @@ int fa_kv_tile(fa_dtype dtype, int d, int pcast)
     if (d != 64 && d != 128) return -1;
     if (dtype == FA_F32) return fa::fwd_f32_kv_tile(d);
     if (pcast) return -1;
-    if (dtype == FA_F16 || dtype == FA_BF16) return fa::fwd_mfma_kv_tile(d);
+    if (dtype == FA_F16 || dtype == FA_BF16) return fa::fwd_mfma_kv_tile(d, 1, 1, 1LL << 30);
     return -1;
 }
 

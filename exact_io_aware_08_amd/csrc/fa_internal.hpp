@@ -44,7 +44,7 @@ constexpr int kFwdQTile = 128;     // fewest queries per forward workgroup (grid
 constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
 
 int fwd_f32_kv_tile(int d);   // keys per KV tile, fp32 / P-cast kernel
-int fwd_mfma_kv_tile(int d);  // keys per KV tile, bf16 / fp16 kernel
+int fwd_mfma_kv_tile(int d, long long B, long long H, long long Nq);  // keys per KV tile, bf16 / fp16 kernel
 int decode_chunk_keys(int d); // granularity of a decode split (keys)
 hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);

@@ -113,7 +113,13 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
                        unsigned long long *counts, void *stream);
 
 /* Keys per KV tile used by the forward kernels for (dtype, d, pcast), or -1
- * for an unsupported combination.  Tile t covers keys [t*B_c, (t+1)*B_c). */
+ * for an unsupported combination.  Tile t covers keys [t*B_c, (t+1)*B_c).
+ * The fp32 / P-cast value is exact (the P-cast result depends on it: a cast
+ * sees the running max of the tiles before it).  For the 16-bit kernels at
+ * d = 64 the width also depends on the grid -- 32 keys when at least 1024
+ * workgroups of 256 query rows exist (ceil(Nq/256)*B*H >= 1024), else 64 --
+ * and this returns the large-grid value; their results depend on it only
+ * through rounding order. */
 int fa_kv_tile(fa_dtype dtype, int d, int pcast);
 
 /*

@@ -146,3 +146,15 @@ def test_lse_optional_and_stream():
     o_ref, _ = oracle.attention(widen(q, "bf16"), widen(k, "bf16"), widen(v, "bf16"), True,
                                 _scale(64))
     compare(o, None, o_ref, None, "bf16", "side stream")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_large_grid_uses_256_row_tiles(causal):
+    """ceil(N/256)*B*H >= 1024 selects the 256-row workgroups (32-key tiles);
+    smaller grids use 128-row workgroups.  Ragged N, GQA, sampled rows that
+    include the last row of every head."""
+    B, H, Hkv, N = 8, 16, 4, 2000
+    assert fa.kv_tile(torch.bfloat16, 64) == 32
+    rows = _sampled_rows(B, H, N, 24)
+    m = run_case(B, H, Hkv, N, N, 64, "bf16", causal, seed=21, rows=rows)
+    assert m["max_abs"] <= 2e-2
