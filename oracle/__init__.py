@@ -82,6 +82,10 @@ def _load():
                               ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
                               ctypes.c_int, _c_i64, _ip, _c_i64, _dp, _dp, _up, ctypes.c_int]
     lib.orc_pcast.restype = ctypes.c_int
+    lib.orc_attention_bwd.argtypes = [_fp, _fp, _fp, _fp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      _c_i64, ctypes.c_int, ctypes.c_double, _dp, _dp, _dp, _dp,
+                                      _dp, _dp, ctypes.c_int]
+    lib.orc_attention_bwd.restype = ctypes.c_int
     lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
     lib.orc_e4m3_encode.restype = ctypes.c_uint
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint]
@@ -153,6 +157,32 @@ def attention(q, k, v, causal: bool, scale: float, rows=None, nthreads: int | No
     if rc != 0:
         raise ValueError(f"orc_attention rejected its arguments (rc={rc})")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, abs_sums: bool = False,
+                  nthreads: int | None = None):
+    """orc_attention_bwd: (dq, dk, dv) in float64 for the loss gradient dout = dL/dO.
+
+    q, dout: [B,H,Nq,d]; k, v: [B,Hkv,Nk,d] (float32 arrays with the exact
+    values handed to the GPU).  With abs_sums=True also returns the absolute
+    sums (adq, adk, adv) of the terms of each gradient element.
+    """
+    lib = _load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dq = np.zeros((B, H, Nq, d), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Nk, d), dtype=np.float64)
+    dv = np.zeros((B, Hkv, Nk, d), dtype=np.float64)
+    ab = [np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)] if abs_sums else [None] * 3
+    rc = lib.orc_attention_bwd(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(dout, _fp), B, H,
+                               Hkv, Nq, Nk, d, int(bool(causal)), float(scale), _ptr(dq, _dp),
+                               _ptr(dk, _dp), _ptr(dv, _dp),
+                               *[None if a is None else _ptr(a, _dp) for a in ab],
+                               nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"orc_attention_bwd rejected its arguments (rc={rc})")
+    return (dq, dk, dv, *ab) if abs_sums else (dq, dk, dv)
 
 
 def attention_probs(q, k, causal: bool, scale: float, b: int, h: int, i: int) -> np.ndarray:

@@ -26,6 +26,9 @@
  *                         Monte Carlo of the model)
  *  orc_expected_max_gauss pinned (k=1 -> 0, k=2 -> 1/sqrt(pi), Monte Carlo)
  *  orc_dp .............. pinned (the two facts printed on [PC] "Optimizacion 2")
+ *  orc_attention_bwd ... pinned (torch fp64 autograd of SDPA, central finite
+ *                         differences of orc_attention, the sum rules
+ *                         sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i)
  */
 #include <math.h>
 #include <pthread.h>
@@ -387,4 +390,128 @@ double orc_dp(double S)
 {
     const double k = ceil(log2(S));
     return ldexp(1.0, (int)k - 4) / S;
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass by its definition.  [MM] "Pase hacia atras: volver a      */
+/* calcular en lugar de almacenar": the forward keeps only O and the row    */
+/* statistics; the gradient is formed from the softmax probabilities again. */
+/* With L a scalar loss and dO = dL/dO given, for each query row i and each */
+/* visible key j (scores s_ij = scale * q_i.k_j, p from the complete row):  */
+/*   dp_ij = dO_i . v_j                       (dL/dp_ij)                    */
+/*   D_i   = sum_j p_ij dp_ij                                               */
+/*   dS_ij = p_ij (dp_ij - D_i)               (softmax Jacobian applied)    */
+/*   dQ_i  = scale * sum_j dS_ij k_j                                        */
+/*   dK_j += scale * dS_ij q_i,   dV_j += p_ij dO_i                         */
+/* With GQA the key/value gradients sum over the query heads of a group.    */
+/* Optional absolute sums (for error bounds of reduced-precision results):  */
+/*   adq = scale sum_j |dS_ij||k_j|, adk = scale sum_i |dS_ij||q_i|,        */
+/*   adv = sum_i p_ij |dO_i|   (elementwise in the head dimension).         */
+/* Work is split over (b, KV head): one thread owns every output row of     */
+/* that KV head and of its query heads, so nothing is shared.               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float *q, *k, *v, *dout;
+    i64 B, H, Hkv, Nq, Nk, d;
+    int causal;
+    double scale;
+    double *dq, *dk, *dv, *adq, *adk, *adv;
+    i64 next;  /* atomic */
+} bjob_t;
+
+static void *bwd_worker(void *arg)
+{
+    bjob_t *J = (bjob_t *)arg;
+    const i64 d = J->d, g = J->H / J->Hkv;
+    double *p = (double *)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
+    job_t F;  /* for visible_count */
+    memset(&F, 0, sizeof F);
+    F.causal = J->causal; F.Nq = J->Nq; F.Nk = J->Nk;
+    for (;;) {
+        const i64 it = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+        if (it >= J->B * J->Hkv) break;
+        const i64 b = it / J->Hkv, hk = it % J->Hkv;
+        const float *kb = J->k + (b * J->Hkv + hk) * J->Nk * d;
+        const float *vb = J->v + (b * J->Hkv + hk) * J->Nk * d;
+        double *dkb = J->dk + (b * J->Hkv + hk) * J->Nk * d;
+        double *dvb = J->dv + (b * J->Hkv + hk) * J->Nk * d;
+        double *adkb = J->adk ? J->adk + (b * J->Hkv + hk) * J->Nk * d : NULL;
+        double *advb = J->adv ? J->adv + (b * J->Hkv + hk) * J->Nk * d : NULL;
+        for (i64 x = 0; x < J->Nk * d; ++x) {
+            dkb[x] = 0.0; dvb[x] = 0.0;
+            if (adkb) adkb[x] = 0.0;
+            if (advb) advb[x] = 0.0;
+        }
+        for (i64 h = hk * g; h < (hk + 1) * g; ++h) {
+            for (i64 i = 0; i < J->Nq; ++i) {
+                const i64 row = (b * J->H + h) * J->Nq + i;
+                const float *qi = J->q + row * d;
+                const float *doi = J->dout + row * d;
+                double *dqi = J->dq + row * d;
+                double *adqi = J->adq ? J->adq + row * d : NULL;
+                for (i64 c = 0; c < d; ++c) {
+                    dqi[c] = 0.0;
+                    if (adqi) adqi[c] = 0.0;
+                }
+                const i64 lim = visible_count(&F, i);
+                if (lim == 0) continue;
+                /* probabilities of the complete row (two passes) */
+                double m = -INFINITY, l = 0.0;
+                for (i64 j = 0; j < lim; ++j) {
+                    p[j] = J->scale * dot(qi, kb + j * d, d);
+                    if (p[j] > m) m = p[j];
+                }
+                for (i64 j = 0; j < lim; ++j) { p[j] = exp(p[j] - m); l += p[j]; }
+                for (i64 j = 0; j < lim; ++j) p[j] /= l;
+                /* dp and D */
+                double D = 0.0;
+                for (i64 j = 0; j < lim; ++j) {
+                    dp[j] = dot(doi, vb + j * d, d);
+                    D += p[j] * dp[j];
+                }
+                for (i64 j = 0; j < lim; ++j) {
+                    const double ds = p[j] * (dp[j] - D);
+                    const float *kj = kb + j * d;
+                    for (i64 c = 0; c < d; ++c) {
+                        dqi[c] += J->scale * ds * (double)kj[c];
+                        dkb[j * d + c] += J->scale * ds * (double)qi[c];
+                        dvb[j * d + c] += p[j] * (double)doi[c];
+                        if (adqi) adqi[c] += J->scale * fabs(ds) * fabs((double)kj[c]);
+                        if (adkb) adkb[j * d + c] += J->scale * fabs(ds) * fabs((double)qi[c]);
+                        if (advb) advb[j * d + c] += p[j] * fabs((double)doi[c]);
+                    }
+                }
+            }
+        }
+    }
+    free(p);
+    free(dp);
+    return NULL;
+}
+
+/* dq: [B,H,Nq,d]; dk, dv: [B,Hkv,Nk,d] (float64).  adq/adk/adv: the same
+ * shapes, or NULL. */
+int orc_attention_bwd(const float *q, const float *k, const float *v, const float *dout, i64 B,
+                      i64 H, i64 Hkv, i64 Nq, i64 Nk, i64 d, int causal, double scale,
+                      double *dq, double *dk, double *dv, double *adq, double *adk,
+                      double *adv, int nthreads)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || H % Hkv || Nq < 0 || Nk < 0 || d < 1) return -1;
+    bjob_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dout = dout; J.B = B; J.H = H; J.Hkv = Hkv; J.Nq = Nq;
+    J.Nk = Nk; J.d = d; J.causal = causal; J.scale = scale; J.dq = dq; J.dk = dk; J.dv = dv;
+    J.adq = adq; J.adk = adk; J.adv = adv;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[started], NULL, bwd_worker, &J) == 0) ++started;
+    bwd_worker(&J);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    return 0;
 }

@@ -453,6 +453,85 @@ def pin_trading_day_workload():
     assert abs(gb - g["score_matrix_gb_printed"]) / g["score_matrix_gb_printed"] < 0.10
 
 
+# --------------------------------------------------------------------------
+# backward ([MM] "Pase hacia atras": P recomputed from the stored statistics)
+# --------------------------------------------------------------------------
+
+def _torch_grads(q, k, v, dout, causal, scale):
+    """fp64 autograd of torch SDPA with an explicit bottom-right mask."""
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = H // Hkv
+    tq = torch.from_numpy(q).double().requires_grad_()
+    tk = torch.from_numpy(k).double().requires_grad_()
+    tv = torch.from_numpy(v).double().requires_grad_()
+    mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq) if causal else None
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), attn_mask=mask,
+        scale=scale)
+    o.backward(torch.from_numpy(dout).double())
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_bwd_torch_autograd():
+    cases = [
+        (2, 4, 2, 37, 37, 16, True, 0.25),
+        (1, 3, 3, 20, 20, 8, False, 0.5),
+        (1, 6, 3, 21, 50, 8, True, 0.4),    # bottom-right mask, Nq < Nk
+        (1, 4, 1, 45, 45, 32, True, 0.177),  # MQA
+    ]
+    for n, (B, H, Hkv, Nq, Nk, d, causal, scale) in enumerate(cases):
+        q, k, v = _inputs(B, H, Hkv, Nq, Nk, d, seed=70 + n)
+        dout = np.random.default_rng(80 + n).standard_normal((B, H, Nq, d)).astype(np.float32)
+        ours = oracle.attention_bwd(q, k, v, dout, causal, scale)
+        ref = _torch_grads(q, k, v, dout, causal, scale)
+        for name, a, b in zip(("dq", "dk", "dv"), ours, ref):
+            assert np.allclose(a, b, rtol=1e-11, atol=1e-11), f"{name} vs torch case {n}"
+
+
+def pin_bwd_finite_differences():
+    """Central differences of L = sum(O * dO) through the forward oracle, on a
+    causal case with Nq > Nk (rows without keys contribute nothing)."""
+    B, H, Hkv, Nq, Nk, d, scale = 1, 2, 1, 7, 5, 4, 0.6
+    q, k, v = _inputs(B, H, Hkv, Nq, Nk, d, seed=91)
+    dout = np.random.default_rng(92).standard_normal((B, H, Nq, d)).astype(np.float32)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, True, scale)
+    h = 2.0 ** -10   # exact in fp32 for these magnitudes
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, True, scale)
+        return float(np.sum(o * dout))
+
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(arr.shape):
+            x0 = arr[idx]
+            arr[idx] = x0 + np.float32(h)
+            lp = loss(q, k, v)
+            arr[idx] = x0 - np.float32(h)
+            lm = loss(q, k, v)
+            arr[idx] = x0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-5 * (1 + abs(grad[idx])), (idx, fd, grad[idx])
+
+
+def pin_bwd_sum_rules():
+    """Adding one vector to every key leaves each softmax row unchanged, so
+    sum_j dK_j = 0; adding one vector to every value adds it to every O row
+    with a visible key, so sum_j dV_j = sum of those dO_i (per KV head)."""
+    B, H, Hkv, Nq, Nk, d = 2, 6, 2, 40, 64, 16
+    q, k, v = _inputs(B, H, Hkv, Nq, Nk, d, seed=93)
+    dout = np.random.default_rng(94).standard_normal((B, H, Nq, d)).astype(np.float32)
+    for causal in (False, True):
+        dq, dk, dv, adq, adk, adv = oracle.attention_bwd(q, k, v, dout, causal, 0.3, abs_sums=True)
+        assert np.abs(dk.sum(axis=2)).max() < 1e-10
+        g = H // Hkv
+        want = dout.astype(np.float64).reshape(B, Hkv, g, Nq, d).sum(axis=(2, 3))
+        assert np.abs(dv.sum(axis=2) - want).max() < 1e-10
+        # the absolute sums bound the gradients (triangle inequality)
+        for a, b in ((dq, adq), (dk, adk), (dv, adv)):
+            assert np.all(np.abs(a) <= b * (1 + 1e-12) + 1e-300)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -36,6 +36,15 @@ MUTANTS = [
     ("e4m3_ties_away", "nearbyint(ldexp(a, 3 - E))", "round(ldexp(a, 3 - E))", 0),
     ("F_sign_of_delta_k", "delta + delta_k - 10.0 * log(2.0) - log(S)", "delta - delta_k - 10.0 * log(2.0) - log(S)", 0),
     ("dp_exponent", "ldexp(1.0, (int)k - 4) / S", "ldexp(1.0, (int)k - 3) / S", 0),
+    ("bwd_no_D", "const double ds = p[j] * (dp[j] - D);", "const double ds = p[j] * dp[j];", 0),
+    ("bwd_dk_unscaled", "dkb[j * d + c] += J->scale * ds * (double)qi[c];",
+     "dkb[j * d + c] += ds * (double)qi[c];", 0),
+    ("bwd_dv_uses_dp", "dvb[j * d + c] += p[j] * (double)doi[c];",
+     "dvb[j * d + c] += dp[j] * (double)doi[c];", 0),
+    ("bwd_dq_uses_v", "dqi[c] += J->scale * ds * (double)kj[c];",
+     "dqi[c] += J->scale * ds * (double)(vb + j * d)[c];", 0),
+    ("bwd_gqa_one_head", "for (i64 h = hk * g; h < (hk + 1) * g; ++h) {",
+     "for (i64 h = hk * g; h < hk * g + 1; ++h) {", 0),
 ]
 
 
