@@ -134,6 +134,36 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
     return o, lse
 
 
+def bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, Nq))
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+        workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """Backward of fwd: (dq, dk, dv) from the forward's o and lse and dout = dL/dO."""
+    B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if t.device != q.device or t.dtype != q.dtype or not t.is_contiguous() or t.shape != shape:
+            raise ValueError(f"{name} must match q (device, dtype, shape, contiguous)")
+    if lse.device != q.device or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be a contiguous fp32 [B, H, Nq] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    if workspace is None:
+        n = bwd_workspace_bytes(B, H, Nq)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Nq,
+                       Nk, d, int(bool(causal)), float(scale), _DT[q.dtype], workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    check(st, "fa_bwd")
+    return dq, dk, dv
+
+
 def cast_e4m3(x, stream=None):
     """Device E4M3 round trip used by the P-cast kernel: (codes uint8, values fp32)."""
     if x.device.type != "cuda" or x.dtype != torch.float32 or not x.is_contiguous():

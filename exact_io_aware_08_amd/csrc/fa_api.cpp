@@ -218,6 +218,41 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq)
+{
+    if (B < 0 || H < 1 || Nq < 0) return 0;
+    return round256((size_t)B * (size_t)H * (size_t)Nq * sizeof(float));
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int H, int Hkv, int Nq,
+                 int Nk, int d, int causal, float scale, fa_dtype dtype, void *workspace,
+                 size_t workspace_bytes, void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale);
+    if (s != FA_OK) return s;
+    // q-side tensors are needed when B*Nq > 0, k-side ones when B*Nk > 0
+    if ((s = check_fwd_ptrs(q, k, v, dq, lse, B, Nq, Nk)) != FA_OK) return s;
+    const bool need_q = B > 0 && Nq > 0, need_kv = B > 0 && Nk > 0;
+    if (need_q && (!o || !dout || !lse)) return FA_ERR_NULL;
+    if (need_kv && (!dk || !dv)) return FA_ERR_NULL;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if ((long long)((Nk + 127) / 128) * B * Hkv > kMaxSlice) return FA_ERR_SHAPE;
+    if (B == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::BwdProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dvec = static_cast<float *>(workspace);
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d;
+    p.causal = causal; p.scale = scale; p.dtype = (int)dtype;
+    return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n, void *stream)
 {
     if (n == 0) return FA_OK;

@@ -46,10 +46,6 @@ namespace {
 constexpr int NW = 4;
 constexpr int WK = 32;                    // keys per wave per step
 static_assert(NW * WK == kDecodeStep, "step");
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9 V# word 3)
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int D> struct DecodeGeo {
     static constexpr int NP = D == 64 ? 4 : 2;  // register stages (steps in flight)
@@ -227,11 +223,8 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int mb = 0; mb < D / 16; ++mb) {
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vt + tr0 + 16 * mb));
-                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vt + tr0 + 16 * VS + 16 * mb));
-                const u32x2_t a = bitcast<u32x2_t>(lo), bq = bitcast<u32x2_t>(hi);
+                const u32x2_t a = read_tr(vt + tr0 + 16 * mb);
+                const u32x2_t bq = read_tr(vt + tr0 + 16 * VS + 16 * mb);
                 acc[mb] = M::mma16(bitcast<v8>(u32x4_t{a.x, a.y, bq.x, bq.y}), pop, acc[mb]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -96,4 +96,30 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9 V# word 3)
+
+// Buffer resource over rows [j0, rows) of a row-major slice of D-element
+// rows: loads past the end read as zero (the hardware range check on the
+// VGPR offset).  All arguments are wave-uniform.
+template <typename T, int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int j0)
+{
+    const int left = rows > j0 ? (rows - j0) * D * (int)sizeof(T) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0, left,
+                                             kBufferFlags);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane s supplies the address
+// of row r0 + s/4, columns c0 + 4(s%4)..+3 of a row-major 16-bit tile, and
+// lane i receives column c0 + i of rows r0..r0+3 (four 16-bit values).
+template <typename T>
+__device__ __forceinline__ u32x2_t read_tr(const T *p)
+{
+    return bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p)));
+}
+
 }  // namespace fa

@@ -53,7 +53,6 @@ namespace fa {
 namespace {
 
 constexpr int NW = 4;         // waves per workgroup
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9 V# word 3)
 
 // Row-sum accumulation of one converted pair of probabilities.  For fp16
 // the sum is taken over the converted values with v_dot2 (an 11-bit
@@ -93,16 +92,6 @@ template <int D, int QB> struct Geo {
     static_assert(VS >= D && (VS * 2) % 16 == 0, "V row stride");
 };
 
-// Buffer resource over rows [j0, rows) of a row-major slice of D-element
-// rows: loads past the end read as zero.  All arguments are wave-uniform.
-template <typename T, int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int j0)
-{
-    const int left = rows > j0 ? (rows - j0) * D * (int)sizeof(T) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0, left,
-                                             kBufferFlags);
-}
-
 // Per-thread offsets of the staging loads and LDS stores within a tile:
 // chunk ci = tid + 256 r -> row ci / CPR, chunk ci % CPR (row-major,
 // coalesced).  K and V use the same map, with their own LDS row strides.
@@ -139,17 +128,6 @@ __device__ __forceinline__ void store_rows(T *buf, const int (&st)[Geo<D, QB>::K
 {
 #pragma unroll
     for (int r = 0; r < Geo<D, QB>::KCH; ++r) *reinterpret_cast<u32x4_t *>(&buf[st[r]]) = reg[r];
-}
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// Four 16-bit values of one column from four consecutive rows (see the
-// transpose-read layout in the kernel comment).
-template <typename T>
-__device__ __forceinline__ u32x2_t read_tr(const T *p)
-{
-    return bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p)));
 }
 
 // S^T blocks (32 keys x 32 queries each) = K_tile Q_wave^T; block index

@@ -39,6 +39,18 @@ struct DecodeProblem {
     float *part_lse;  // [B, H, splits]     (splits > 1)
 };
 
+// Backward problem (16-bit types).  dvec: [B, H, Nq] fp32 scratch for D.
+struct BwdProblem {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *dvec;
+    int B, H, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+    int dtype;
+};
+
 // Tile constants shared by the launchers and fa_kv_tile().
 constexpr int kFwdQTile = 128;     // fewest queries per forward workgroup (grid-size bound)
 constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
@@ -49,6 +61,7 @@ int decode_chunk_keys(int d); // granularity of a decode split (keys)
 hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeProblem &p, hipStream_t stream);
+hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n,
                             hipStream_t stream);
 

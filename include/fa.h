@@ -157,6 +157,28 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
                     void *stream);
 
 /*
+ * Backward pass by recomputation (marketmaker.cc, section "Pase hacia atras:
+ * volver a calcular en lugar de almacenar"): from the forward's O and LSE
+ * and the output gradient dout = dL/dO, the gradients
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dout,
+ * with P = exp(scale Q K^T - LSE), dS = P (dout V^T - D), D = rowsum(dout * O),
+ * recomputing P tile by tile.  GQA: dk, dv sum over the query heads of a group.
+ *   q, o, dout, dq: device [B, H, Nq, d];  k, v, dk, dv: device [B, Hkv, Nk, d];
+ *   lse: device [B, H, Nq] fp32 as written by fa_fwd (natural log; -inf for a
+ *   row without visible keys).  Gradients are written in `dtype`; every
+ *   element of dq, dk and dv is written (zeros where no key/query is visible).
+ *   dtype: FA_BF16 or FA_F16.  Same causal convention as fa_fwd.
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(B, H, Nq)
+ *   bytes (holds D), 16-byte aligned; contents on entry do not matter.
+ *   Results are deterministic (no floating-point atomics).
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int H, int Hkv, int Nq,
+                 int Nk, int d, int causal, float scale, fa_dtype dtype, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
  * The device E4M3 round trip that fa_fwd_pcast applies to p_scale * P, on n
  * fp32 values: codes[i] = E4M3_RNE(x[i]) (OCP E4M3FN bit pattern),
  * back[i] = the value of that code.  x, codes, back are device pointers

@@ -151,3 +151,33 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x)
+
+
+def _bwd(ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=2, Nq=64, Nk=64,
+             d=64, causal=1, scale=0.125, dtype=BF16, ws=P)
+    a.update(kw)
+    need = fa.bwd_workspace_bytes(a["B"], a["H"], a["Nq"])
+    return fa.load().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                            a["causal"], a["scale"], a["dtype"], a["ws"],
+                            need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), "FA_ERR_NULL"), (dict(do=None), "FA_ERR_NULL"), (dict(lse=None), "FA_ERR_NULL"),
+    (dict(o=None), "FA_ERR_NULL"), (dict(dk=None), "FA_ERR_NULL"), (dict(dv=None), "FA_ERR_NULL"),
+    (dict(dq=None), "FA_ERR_NULL"), (dict(do=PM), "FA_ERR_ALIGN"), (dict(dv=PM), "FA_ERR_ALIGN"),
+    (dict(ws=None), "FA_ERR_WORKSPACE"), (dict(ws_bytes=8), "FA_ERR_WORKSPACE"),
+    (dict(ws=PM), "FA_ERR_ALIGN"), (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(d=32), "FA_ERR_HEADDIM"),
+    (dict(H=6, Hkv=4), "FA_ERR_GQA"), (dict(scale=0.0), "FA_ERR_SCALE"), (dict(causal=3), "FA_ERR_ARG"),
+    (dict(B=-1), "FA_ERR_SHAPE"), (dict(B=0), "FA_OK"), (dict(Nq=0, Nk=0), "FA_OK"),
+])
+def test_bwd_validation(kw, expect):
+    assert _bwd(**kw) == S[expect]
+
+
+def test_bwd_workspace_size():
+    assert fa.bwd_workspace_bytes(2, 3, 100) == 2560   # 600 floats, rounded up to 256 bytes
+    assert fa.bwd_workspace_bytes(0, 3, 100) == 0
+    assert fa.bwd_workspace_bytes(-1, 3, 100) == 0
