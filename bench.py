@@ -186,6 +186,20 @@ def main():
                                        "tflops": round(f2 / (ms2 * 1e-3) / 1e12, 1),
                                        "frac_of_bf16_peak": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                        "shape": [4, 12, 2048, 64], "causal": True}
+        # backward by recomputation on the trading-day prefill (GPU forward's O, LSE)
+        g3 = torch.empty_like(q3).normal_(generator=torch.Generator(device=dev).manual_seed(0))
+        ws3 = torch.empty(max(fa.bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8, device=dev)
+        dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+        fa.fwd(q3, k3, v3, causal=True, scale=c3["scale"], out=o3, lse=l3)
+        msb = _timed(lambda i: fa.bwd(q3, k3, v3, o3, g3, l3, causal=True, scale=c3["scale"],
+                                      workspace=ws3, dq=dq3, dk=dk3, dv=dv3), 10, 5, torch)
+        fb = 2.5 * flops   # 10d per visible pair: 5 products against the forward's 2
+        extra["trading_day_bwd_bf16"] = {"ms_per_call": round(msb, 4),
+                                         "tflops": round(fb / (msb * 1e-3) / 1e12, 1),
+                                         "frac_of_bf16_peak": round(fb / (msb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                         "algorithmic_flop": fb,
+                                         "note": "dQ, dK, dV from the forward's O and LSE; D, dQ and dK/dV kernels"}
+        del g3, ws3, dq3, dk3, dv3
         # P-cast on the attention-sink workload: flush counters and time per run
         c5 = fagen.CONFIGS[5]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
