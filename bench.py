@@ -71,6 +71,62 @@ def _timed(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def _sweep(torch, fa, fagen, to_dev, dev):
+    """Sequence-length sweep of [MM] "La medicion" at the op level: the
+    trading-model inputs (AR(1) + noise, 12 heads, d = 64, causal, bf16) at
+    N = 512, 4,096 and 32,768.  For each N: fa_fwd and fa_fwd + fa_bwd time and
+    the extra device memory each call allocates, against the materialised
+    definition (scores, softmax and P V as separate bf16 tensor ops, the
+    standard path of [MM] "Por que la atencion esta ligada a la memoria"),
+    forward only."""
+    res = {"metric": "op cost vs sequence length (fa_fwd / fa_bwd vs materialised attention)",
+           "data": "synthetic AR(1) phi=0.9 + N(0,0.1), seed 0", "dtype": "bf16", "rows": []}
+    for N in (512, 4096, 32768):
+        cfg = dict(B=1, H=12, Hkv=12, Nq=N, Nk=N, d=64, dtype="bf16", kind="ar1")
+        qn, kn, vn = fagen.make_inputs(cfg, 0)
+        q, k, v = (to_dev(x, "bf16") for x in (qn, kn, vn))
+        scale = 0.125
+        flops = 2.0 * 64 * 12 * N * (N + 1)
+        row = {"N": N, "score_matrix_bytes_bf16": 12 * N * N * 2}
+
+        def peak(fn):
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            r = fn()
+            torch.cuda.synchronize()
+            return r, torch.cuda.max_memory_allocated() - base
+
+        it = max(3, min(200, int(2e12 / flops)))
+        (o, lse), mem_f = peak(lambda: fa.fwd(q, k, v, causal=True, scale=scale))
+        ms_f = _timed(lambda i: fa.fwd(q, k, v, causal=True, scale=scale), it, 3, torch)
+        g = torch.empty_like(q).normal_(generator=torch.Generator(device=dev).manual_seed(1))
+        _, mem_b = peak(lambda: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale))
+        ms_b = _timed(lambda i: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale), it, 3, torch)
+        row["fa_fwd"] = {"ms": round(ms_f, 4), "tflops": round(flops / (ms_f * 1e-3) / 1e12, 1),
+                         "extra_bytes": int(mem_f)}
+        row["fa_bwd"] = {"ms": round(ms_b, 4), "tflops": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 1),
+                         "extra_bytes": int(mem_b)}
+        kt = k.transpose(-1, -2).contiguous()
+        mask = torch.ones(N, N, dtype=torch.bool, device=dev).triu(1)
+
+        def materialised():
+            sc = torch.matmul(q, kt) * scale
+            sc.masked_fill_(mask, float("-inf"))
+            return torch.matmul(torch.softmax(sc, dim=-1), v)
+
+        om, mem_m = peak(materialised)
+        ms_m = _timed(lambda i: materialised(), max(3, it // 4), 2, torch)
+        row["materialised_fwd"] = {"ms": round(ms_m, 4), "extra_bytes": int(mem_m),
+                                   "max_abs_diff_vs_fa_fwd": float((om.float() - o.float()).abs().max())}
+        row["fwd_speedup"] = round(ms_m / ms_f, 2)
+        row["fwd_memory_ratio"] = round(mem_m / max(mem_f, 1), 1)
+        res["rows"].append(row)
+        del q, k, v, kt, mask, o, lse, g, om
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +137,10 @@ def main():
                     help="oracle rows per head for the CPU leg (0: every row, about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: sequence-length sweep N in {512, 4096, 32768} "
+                         "(B=1, H=12, d=64, bf16, causal, AR(1) inputs): time and peak device "
+                         "memory of fa_fwd (+ fa_bwd) against materialised attention")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (tiny fp32, GPT-2-small prefill, P-cast sink)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -106,6 +166,10 @@ def main():
         if dt == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.sweep:
+        print(json.dumps(_sweep(torch, fa, fagen, to_dev, dev)))
+        return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
