@@ -222,6 +222,35 @@ def main():
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": _traffic("fa_decode_gqa_bf16_pmc.md", DECODE_KERNEL),
                             "timed": "sweep + merge kernels per call"}}
+        # the same caches scattered over randomly permuted 128-key pages, at
+        # full length and at seeded ragged lengths (uniform in [1, Nk])
+        ps = 128
+        npg = Nk4 // ps
+        gen = torch.Generator(device="cpu").manual_seed(0)
+        perm = torch.randperm(B4 * npg, generator=gen)
+        table = perm.view(B4, npg).to(torch.int32).to(dev)
+        pcaches = []
+        for kc, vc in caches:
+            def pages(x):
+                x = x.view(B4, Hkv4, npg, ps, d4).permute(0, 2, 1, 3, 4).reshape(B4 * npg, Hkv4, ps, d4)
+                y = torch.empty_like(x)
+                y[perm.to(dev)] = x
+                return y
+            pcaches.append((pages(kc), pages(vc)))
+        paged = {"page_size": ps}
+        lens_full = torch.full((B4,), Nk4, dtype=torch.int32, device=dev)
+        lens_rag = torch.randint(1, Nk4 + 1, (B4,), generator=gen, dtype=torch.int32)
+        for name, lens in (("full", lens_full), ("ragged", lens_rag.to(dev))):
+            pus = 1e3 * _timed(lambda i: fa.decode_paged(q4, pcaches[i % 4][0], pcaches[i % 4][1],
+                                                         table, lens, scale=c4["scale"],
+                                                         workspace=ws, out=o4, lse=l4),
+                               args.decode_steps, 400, torch)
+            kv_keys = int(lens.sum().item())
+            pbytes = 2 * Hkv4 * kv_keys * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4
+            paged[name] = {"us_per_call": round(pus, 2), "keys": kv_keys,
+                           "GB/s": round(pbytes / (pus * 1e-6) / 1e9, 1)}
+        dec["paged"] = paged
+        del pcaches
         if args.only == "decode":
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
                         "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})

@@ -164,6 +164,43 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     return dq, dk, dv
 
 
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None,
+                 num_splits: int = 0, workspace=None, out=None, lse=None, stream=None):
+    """Decode against a paged cache.  q: [B,H,1,d]; k_pages, v_pages:
+    [num_pages,Hkv,page_size,d]; block_table: int32 [B,max_pages];
+    seq_lens: int32 [B]."""
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _check_tensor(n, t, 4)
+    if not (q.dtype == k_pages.dtype == v_pages.dtype) or k_pages.shape != v_pages.shape:
+        raise ValueError("q, k_pages, v_pages: one dtype; k_pages and v_pages one shape")
+    B, H, Nq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pages.shape
+    if Nq != 1 or dk != d:
+        raise ValueError("decode takes one query token per (batch, head) with the cache's d")
+    for n, t, shape in (("block_table", block_table, None), ("seq_lens", seq_lens, (B,))):
+        if t.device != q.device or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 tensor on q's device")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = decode_workspace(B, H, Hkv, max_pages * page_size, d, num_splits, q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    st = load().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                block_table.data_ptr(), seq_lens.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, H, Hkv, num_pages, page_size, max_pages, d,
+                                float(scale), _DT[q.dtype], int(num_splits),
+                                workspace.data_ptr() if workspace is not None else None,
+                                workspace.numel() * workspace.element_size()
+                                if workspace is not None else 0, _stream_ptr(stream))
+    check(st, "fa_decode_paged")
+    return o, lse
+
+
 def cast_e4m3(x, stream=None):
     """Device E4M3 round trip used by the P-cast kernel: (codes uint8, values fp32)."""
     if x.device.type != "cuda" or x.dtype != torch.float32 or not x.is_contiguous():

@@ -36,6 +36,8 @@ SIGNATURES = {
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "fa_cast_e4m3": (_i, [_vp, _vp, _vp, _sz, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                             _i, _i, _vp, _sz, _vp]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                     _i, _vp, _sz, _vp]),
     "fa_status_str": (ctypes.c_char_p, [_i]),

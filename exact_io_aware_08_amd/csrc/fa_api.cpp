@@ -218,6 +218,52 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int *block_table, const int *seq_lens, void *o, float *lse,
+                          int B, int H, int Hkv, int num_pages, int page_size, int max_pages,
+                          int d, float scale, fa_dtype dtype, int num_splits, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || num_pages < 0 || max_pages < 1 || page_size < 32 || page_size % 32 != 0)
+        return B < 0 ? FA_ERR_SHAPE : FA_ERR_ARG;
+    const long long max_seq = (long long)max_pages * page_size;
+    if (max_seq > kMaxSlice / 128) return FA_ERR_SHAPE;
+    if ((long long)num_pages * Hkv * page_size * d > (1LL << 40)) return FA_ERR_SHAPE;
+    fa_status s = check_fwd_shape(B, H, Hkv, 1, (int)max_seq, d, scale);
+    if (s != FA_OK) return s;
+    if (B > 0 && (!q || !o || !block_table || !seq_lens)) return FA_ERR_NULL;
+    if (B > 0 && num_pages > 0 && (!k_pages || !v_pages)) return FA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return FA_ERR_ALIGN;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
+    const int splits = fa_decode_splits(B, H, Hkv, (int)max_seq, num_splits);
+    const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits);
+    if (lay.total > 0 && (!workspace || workspace_bytes < lay.total)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const long long blocks = (long long)splits * B * Hkv * ((H / Hkv + 15) / 16);
+    if (blocks > kMaxSlice) return FA_ERR_SHAPE;
+    if (B == 0) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::DecodeProblem p{};
+    p.q = q; p.k = k_pages; p.v = v_pages; p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nk = (int)max_seq; p.d = d; p.scale = scale;
+    p.dtype = (int)dtype;
+    p.splits = splits;
+    p.chunk = decode_chunk((int)max_seq, splits, d);
+    if (lay.total > 0) {
+        char *ws = static_cast<char *>(workspace);
+        p.part_lse = reinterpret_cast<float *>(ws + lay.lse_off);
+        p.part_o = reinterpret_cast<float *>(ws + lay.o_off);
+    }
+    p.block_table = block_table; p.seq_lens = seq_lens;
+    p.page_size = page_size; p.max_pages = max_pages; p.num_pages = num_pages;
+    return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq)
 {
     if (B < 0 || H < 1 || Nq < 0) return 0;

@@ -37,6 +37,12 @@
 //     column i of keys kb..kb+3 -- exactly the A-operand slots.
 // Each of the 4 waves takes its own 32 keys of every 128-key step, keeps its
 // own (m, l, O), and the waves are merged through LDS at the end.
+//
+// The cache is either contiguous or paged with per-sequence lengths (a
+// block table maps each sequence's logical pages to physical pages, the
+// KV-cache management of serving systems the "FlashAttention (IT)" entry
+// mentions under "Soluzioni specializzate"); only the address of each
+// wave's 32-key block changes.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -63,12 +69,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, in
                                              bytes > 0 ? bytes : 0, kBufferFlags);
 }
 
-template <typename T, int D>
+// Cache addressing.  Contiguous: [B, Hkv, Nk, D], every sequence Nk keys.
+// Paged: K/V pages [num_pages, Hkv, page_size, D]; key t of sequence b lives
+// in page block_table[b * max_pages + t / page_size] at row t % page_size,
+// and the sequence has seq_lens[b] keys.  page_size is a multiple of 32, so
+// the 32 keys a wave loads per step never straddle a page.  Lengths are
+// clamped to [0, max_pages * page_size] and a page index outside
+// [0, num_pages) reads nothing, so bad tables cannot make an access fault.
+struct PagedCache {
+    const int *block_table;
+    const int *seq_lens;
+    int page_size, max_pages, num_pages;
+};
+
+template <typename T, int D, bool PAGED>
 __global__ void __launch_bounds__(256)
 decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__restrict__ V,
               T *__restrict__ O, float *__restrict__ LSE, float *__restrict__ part_o,
               float *__restrict__ part_lse, int H, int Hkv, int Nk, int G, int n_qgroups,
-              int splits, int chunk, float scale, float scale_log2)
+              int splits, int chunk, float scale, float scale_log2, PagedCache pc)
 {
     using M = Mma16<T>;
     using v8 = typename M::v8;
@@ -96,9 +115,11 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     const int h0 = hk * G + qg * 16;
     const int nq = min(16, G - qg * 16);  // real query heads in this group
 
+    int nk_b = Nk;
+    if (PAGED) nk_b = max(0, min(pc.seq_lens[b], pc.max_pages * pc.page_size));
     const int kbeg = split * chunk;
-    const int kend = min(Nk, kbeg + chunk);
-    const size_t kvoff = (size_t)bk * Nk * D;
+    const int kend = min(nk_b, kbeg + chunk);
+    const size_t kvoff = PAGED ? 0 : (size_t)bk * Nk * D;
     const T *Kb = K + kvoff;
     const T *Vb = V + kvoff;
 
@@ -132,9 +153,20 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     const int nsteps = kend > kbeg ? (kend - kbeg + kDecodeStep - 1) / kDecodeStep : 0;
     auto load_step = [&](int sp, int st) {
         const int rel = st * kDecodeStep + w * WK;  // first key of this wave's 32, in the slice
-        const int left = (kend - kbeg - rel) * D * (int)sizeof(T);
-        const __amdgpu_buffer_rsrc_t rk = span_rsrc(Kb + (size_t)(kbeg + rel) * D, left);
-        const __amdgpu_buffer_rsrc_t rv = span_rsrc(Vb + (size_t)(kbeg + rel) * D, left);
+        int left = (kend - kbeg - rel) * D * (int)sizeof(T);
+        size_t row0 = (size_t)(kbeg + rel) * D;  // element offset of the block's first key
+        if (PAGED) {
+            // wave-uniform: one table entry per 32-key block (scalar load)
+            const int t = kbeg + rel;
+            const int pidx = min(t / pc.page_size, pc.max_pages - 1);
+            const int phys = pc.block_table[(size_t)b * pc.max_pages + pidx];
+            const int in_page = t - pidx * pc.page_size;
+            const bool ok = t < kend && (unsigned)phys < (unsigned)pc.num_pages;
+            left = ok ? min(kend - t, pc.page_size - in_page) * D * (int)sizeof(T) : 0;
+            row0 = ok ? ((size_t)phys * Hkv + hk) * pc.page_size * D + (size_t)in_page * D : 0;
+        }
+        const __amdgpu_buffer_rsrc_t rk = span_rsrc(Kb + row0, left);
+        const __amdgpu_buffer_rsrc_t rv = span_rsrc(Vb + row0, left);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -352,11 +384,19 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
     const int G = p.H / p.Hkv;
     const int n_qgroups = (G + 15) / 16;
     const unsigned n_blocks = (unsigned)p.splits * (unsigned)(p.B * p.Hkv * n_qgroups);
-    hipLaunchKernelGGL((decode_kernel<T, D>), dim3(n_blocks), dim3(256), 0, st,
-                       static_cast<const T *>(p.q), static_cast<const T *>(p.k),
-                       static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.part_o,
-                       p.part_lse, p.H, p.Hkv, p.Nk, G, n_qgroups, p.splits, p.chunk, p.scale,
-                       p.scale * kLog2e);
+    const PagedCache pc{p.block_table, p.seq_lens, p.page_size, p.max_pages, p.num_pages};
+    if (p.block_table != nullptr)
+        hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(n_blocks), dim3(256), 0, st,
+                           static_cast<const T *>(p.q), static_cast<const T *>(p.k),
+                           static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.part_o,
+                           p.part_lse, p.H, p.Hkv, p.Nk, G, n_qgroups, p.splits, p.chunk, p.scale,
+                           p.scale * kLog2e, pc);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3(n_blocks), dim3(256), 0, st,
+                           static_cast<const T *>(p.q), static_cast<const T *>(p.k),
+                           static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.part_o,
+                           p.part_lse, p.H, p.Hkv, p.Nk, G, n_qgroups, p.splits, p.chunk, p.scale,
+                           p.scale * kLog2e, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int BH = p.B * p.H;

@@ -37,6 +37,10 @@ struct DecodeProblem {
     int chunk;   // keys per split, multiple of decode_chunk_keys(d)
     float *part_o;    // [B, H, splits, d]  (splits > 1)
     float *part_lse;  // [B, H, splits]     (splits > 1)
+    // paged cache (block_table == nullptr: contiguous [B, Hkv, Nk, d])
+    const int *block_table;  // [B, max_pages]
+    const int *seq_lens;     // [B]
+    int page_size, max_pages, num_pages;
 };
 
 // Backward problem (16-bit types).  dvec: [B, H, Nq] fp32 scratch for D.

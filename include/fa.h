@@ -157,6 +157,31 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
                     void *stream);
 
 /*
+ * Split-KV decode against a paged KV cache with per-sequence lengths (the
+ * KV-cache management of serving systems, systems-analysis.info
+ * "FlashAttention (IT)", section "Soluzioni specializzate").  Same
+ * computation and merge as fa_decode, sequence b attending to its own
+ * seq_lens[b] keys.
+ *   k_pages, v_pages: device [num_pages, Hkv, page_size, d] (dtype).
+ *   block_table: device int32 [B, max_pages]; key t of sequence b is row
+ *     t % page_size of page block_table[b][t / page_size].
+ *   seq_lens: device int32 [B], each in [0, max_pages * page_size]; a
+ *     sequence of length 0 gets O = 0 and LSE = -inf.
+ *   page_size: a multiple of 32, at least 32.  max_pages >= 1.
+ *   The device tables are not read on the host: lengths outside the range
+ *   are clamped and page indices outside [0, num_pages) read nothing, so a
+ *   bad table gives wrong numbers but no out-of-bounds access.
+ *   num_splits, workspace: as fa_decode with Nk = max_pages * page_size
+ *   (size from fa_decode_workspace_bytes(B, H, Hkv, max_pages * page_size,
+ *   d, num_splits)).
+ */
+fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int *block_table, const int *seq_lens, void *o, float *lse,
+                          int B, int H, int Hkv, int num_pages, int page_size, int max_pages,
+                          int d, float scale, fa_dtype dtype, int num_splits, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * Backward pass by recomputation (marketmaker.cc, section "Pase hacia atras:
  * volver a calcular en lugar de almacenar"): from the forward's O and LSE
  * and the output gradient dout = dL/dO, the gradients

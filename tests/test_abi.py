@@ -181,3 +181,26 @@ def test_bwd_workspace_size():
     assert fa.bwd_workspace_bytes(2, 3, 100) == 2560   # 600 floats, rounded up to 256 bytes
     assert fa.bwd_workspace_bytes(0, 3, 100) == 0
     assert fa.bwd_workspace_bytes(-1, 3, 100) == 0
+
+
+def _paged(**kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, H=8, Hkv=2, num_pages=10, page_size=64,
+             max_pages=4, d=64, scale=0.125, dtype=BF16, splits=0, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return fa.load().fa_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["o"], a["lse"],
+                                     a["B"], a["H"], a["Hkv"], a["num_pages"], a["page_size"],
+                                     a["max_pages"], a["d"], a["scale"], a["dtype"], a["splits"],
+                                     a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(page_size=48), "FA_ERR_ARG"), (dict(page_size=16), "FA_ERR_ARG"),
+    (dict(max_pages=0), "FA_ERR_ARG"), (dict(num_pages=-1), "FA_ERR_ARG"),
+    (dict(bt=None), "FA_ERR_NULL"), (dict(sl=None), "FA_ERR_NULL"), (dict(kp=None), "FA_ERR_NULL"),
+    (dict(bt=0x10002), "FA_ERR_ALIGN"), (dict(o=PM), "FA_ERR_ALIGN"),
+    (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(H=6, Hkv=4), "FA_ERR_GQA"), (dict(d=96), "FA_ERR_HEADDIM"),
+    (dict(splits=2, ws=None, ws_bytes=0), "FA_ERR_WORKSPACE"), (dict(B=-2), "FA_ERR_SHAPE"),
+    (dict(B=0), "FA_OK"),
+])
+def test_decode_paged_validation(kw, expect):
+    assert _paged(**kw) == S[expect]

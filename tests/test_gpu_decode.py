@@ -114,3 +114,88 @@ def test_workspace_reuse_across_shapes():
         o_ref, lse_ref = oracle.attention(widen(q, "bf16"), widen(k, "bf16"), widen(v, "bf16"),
                                           False, 0.125)
         compare(o, lse, o_ref, lse_ref, "bf16", "decode reuse")
+
+
+def _paged_case(B, H, Hkv, lens, page_size, d, dt, seed, extra_pages=3):
+    """Seeded contiguous K/V per sequence, scattered over randomly permuted
+    pages.  Returns device tensors and the per-sequence host arrays."""
+    max_len = max(max(lens), 1)
+    max_pages = (max_len + page_size - 1) // page_size
+    need = sum((L + page_size - 1) // page_size for L in lens)
+    num_pages = need + extra_pages
+    cfg = dict(B=B, H=H, Hkv=Hkv, Nq=1, Nk=max_pages * page_size, d=d, dtype=dt, kind="iid")
+    q, k, v = fagen.make_inputs(cfg, seed)
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(num_pages)
+    table = np.full((B, max_pages), -7, np.int32)   # entries past a sequence stay invalid
+    kp = np.zeros((num_pages, Hkv, page_size, d), k.dtype)
+    vp = np.zeros_like(kp)
+    nxt = 0
+    for b, L in enumerate(lens):
+        for pg in range((L + page_size - 1) // page_size):
+            phys = int(perm[nxt]); nxt += 1
+            table[b, pg] = phys
+            rows = slice(pg * page_size, (pg + 1) * page_size)
+            kp[phys] = k[b, :, rows]
+            vp[phys] = v[b, :, rows]
+    return q, k, v, kp, vp, table, max_pages, num_pages
+
+
+@pytest.mark.parametrize("page_size", [32, 128, 256])
+def test_paged_varlen_matches_oracle(page_size):
+    need_gpu()
+    B, H, Hkv, d, dt = 6, 8, 2, 64, "bf16"
+    lens = [0, 1, 33, 700, 1024, 1500]
+    announce(f"fa_decode_paged page_size={page_size} lens={lens}")
+    q, k, v, kp, vp, table, max_pages, num_pages = _paged_case(B, H, Hkv, lens, page_size, d, dt,
+                                                                 seed=page_size)
+    scale = 0.125
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=scale)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        o_b = o[b:b + 1]
+        if L == 0:
+            assert torch.all(o_b == 0) and torch.all(torch.isneginf(lse[b]))
+            continue
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, scale)
+        compare(o_b, lse[b:b + 1], o_ref, l_ref, dt, f"paged b={b} L={L}")
+
+
+@pytest.mark.parametrize("dt,d", [("f16", 64), ("bf16", 128)])
+def test_paged_dtypes_and_head_dims(dt, d):
+    need_gpu()
+    B, H, Hkv = 3, 16, 4
+    lens = [257, 64, 999]
+    announce(f"fa_decode_paged {dt} d={d}")
+    q, k, v, kp, vp, table, _, _ = _paged_case(B, H, Hkv, lens, 64, d, dt, seed=d + 1)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=scale)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, scale)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, dt, f"paged {dt} d={d} b={b}")
+
+
+def test_paged_full_length_equals_contiguous_and_clamps():
+    """Every sequence at the full length: the paged path reads the same keys
+    in the same order as fa_decode on the contiguous cache (identical bits);
+    a length above max_pages * page_size is clamped to it."""
+    need_gpu()
+    B, H, Hkv, d, ps = 4, 8, 2, 64, 128
+    L = 1024
+    announce("fa_decode_paged vs fa_decode, full length")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, [L] * B, ps, d, "bf16", seed=4)
+    dq, dk, dv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    splits = fa.decode_splits(B, H, Hkv, L)
+    o1, l1 = fa.decode(dq, dk, dv, scale=0.125, num_splits=splits)
+    lens = torch.tensor([L, L + 5, L, 1 << 30], dtype=torch.int32, device="cuda")
+    o2, l2 = fa.decode_paged(dq, to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                             torch.from_numpy(table).cuda(), lens, scale=0.125, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
