@@ -86,6 +86,9 @@ def _load():
                                       _c_i64, ctypes.c_int, ctypes.c_double, _dp, _dp, _dp, _dp,
                                       _dp, _dp, ctypes.c_int]
     lib.orc_attention_bwd.restype = ctypes.c_int
+    lib.orc_quant_e4m3.argtypes = [_fp, _c_i64, _c_i64, _c_i64, _c_i64, _fp, ctypes.c_int,
+                                   ctypes.c_int, ctypes.POINTER(ctypes.c_ubyte), _fp]
+    lib.orc_quant_e4m3.restype = ctypes.c_int
     lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
     lib.orc_e4m3_encode.restype = ctypes.c_uint
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint]
@@ -224,6 +227,46 @@ def pcast_emulate(q, k, v, causal: bool, scale: float, kv_tile: int, p_scale: fl
     if rc != 0:
         raise ValueError(f"orc_pcast rejected its arguments (rc={rc})")
     return o, lse, [int(c) for c in counts]
+
+
+def quant_e4m3(x, signs=None, layout: str = "rows32", whole: bool = False):
+    """orc_quant_e4m3: E4M3 codes (uint8, x's shape) and power-of-two scales.
+
+    x: [B,H,N,d] (float32 array of the exact input values).  signs: None or a
+    length-d array of +-1 (random-sign Hadamard rotation before quantising).
+    layout "rows32": scales [B,H,ceil(N/32)]; "channels": scales [B,H,d].
+    whole=True: one scale for the whole tensor, repeated in that layout.
+    """
+    lib = _load()
+    x = _f32(x)
+    B, H, N, d = x.shape
+    lay = {"rows32": 0, "channels": 1}[layout]
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros((B, H, (N + 31) // 32 if lay == 0 else d), dtype=np.float32)
+    sg = None if signs is None else _f32(signs)
+    rc = lib.orc_quant_e4m3(_ptr(x, _fp), B, H, N, d, None if sg is None else _ptr(sg, _fp), lay,
+                            int(bool(whole)), codes.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+                            _ptr(scales, _fp))
+    if rc != 0:
+        raise ValueError(f"orc_quant_e4m3 rejected its arguments (rc={rc})")
+    return codes, scales
+
+
+def dequant_e4m3(codes, scales, layout: str = "rows32") -> np.ndarray:
+    """The values the codes stand for: decode(code) * scale of its group (float32, exact)."""
+    vals = e4m3_decode_table()[np.asarray(codes, dtype=np.int64)]
+    sc = np.asarray(scales, dtype=np.float32)
+    if layout == "rows32":
+        N = vals.shape[2]
+        s = np.repeat(sc, 32, axis=2)[:, :, :N, None]
+    else:
+        s = sc[:, :, None, :]
+    return (vals * s).astype(np.float32)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """decode() of all 256 codes (float32)."""
+    return e4m3_decode(np.arange(256))
 
 
 def e4m3_encode(x) -> np.ndarray:

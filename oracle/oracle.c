@@ -29,6 +29,10 @@
  *  orc_attention_bwd ... pinned (torch fp64 autograd of SDPA, central finite
  *                         differences of orc_attention, the sum rules
  *                         sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i)
+ *  orc_quant_e4m3 ...... pinned (the explicit Sylvester-Hadamard matrix on
+ *                         exactly representable inputs, brute-force search
+ *                         of the minimal scale exponent, half-ulp round trip,
+ *                         exact codes on the E4M3 grid, group layouts)
  */
 #include <math.h>
 #include <pthread.h>
@@ -513,5 +517,94 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
         if (pthread_create(&th[started], NULL, bwd_worker, &J) == 0) ++started;
     bwd_worker(&J);
     for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 (E4M3) quantisation with incoherent processing.                      */
+/*                                                                          */
+/* [MM] "FA3: Mecanica de la tolva", item 3: FP8 attention loses accuracy   */
+/* to outliers; the remedy is to rotate the vectors at random before the    */
+/* block-wise quantisation, so an outlier's magnitude is spread over all    */
+/* coordinates.  The pages give no rotation, block shape or scale rule;     */
+/* the readings taken here:                                                 */
+/*  - rotation: y = H_d (s o x), H_d the Sylvester-Hadamard matrix          */
+/*    (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]) and s a vector of       */
+/*    random signs (+-1).  H_d^T H_d = d I, so applying the same rotation   */
+/*    to q and k multiplies every dot product by exactly d (the attention   */
+/*    scale is divided by d).  H_d x is formed by the fast transform in     */
+/*    fp32, in stages h = 1, 2, 4, ..., d/2, each replacing the pair        */
+/*    (y_j, y_{j+h}) (j mod 2h < h) by (y_j + y_{j+h}, y_j - y_{j+h});      */
+/*    the codes depend on this fp32 rounding, so its order is part of the   */
+/*    definition.                                                           */
+/*  - groups: layout 0 = 32 consecutive rows of one (b, h) (all d columns), */
+/*    scales [B, H, ceil(N/32)]; layout 1 = one column c of one (b, h) over */
+/*    all N rows, scales [B, H, d]; whole != 0 = one group for the entire   */
+/*    tensor, its scale written into every slot of the chosen layout.      */
+/*  - scale: the power of two 2^e with e the smallest integer >= -126 such  */
+/*    that amax <= 448 * 2^e (448 = the largest finite E4M3 value, [PC]    */
+/*    "Optimizacion 2"); a zero group gets e = -126.                        */
+/*  - code = E4M3_RNE(y * 2^-e) (the codec above); dequantised value        */
+/*    decode(code) * 2^e.  Inputs are finite.                               */
+/* ------------------------------------------------------------------------ */
+
+static void fwht_f32(float *y, i64 d)
+{
+    for (i64 h = 1; h < d; h *= 2)
+        for (i64 j = 0; j < d; ++j)
+            if ((j % (2 * h)) < h) {
+                const float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+}
+
+static int scale_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return -126;
+    int E2;
+    const double f = frexp((double)amax, &E2);   /* amax = f * 2^E2, f in [0.5, 1) */
+    /* amax <= 448 * 2^e  <=>  f * 2^E2 <= 0.875 * 2^(9 + e) */
+    int e = (f <= 0.875) ? E2 - 9 : E2 - 8;
+    return e < -126 ? -126 : e;
+}
+
+int orc_quant_e4m3(const float *x, i64 B, i64 H, i64 N, i64 d, const float *signs, int layout,
+                   int whole, unsigned char *codes, float *scales)
+{
+    if (B < 0 || H < 1 || N < 0 || d < 1 || (layout != 0 && layout != 1)) return 1;
+    if (signs && (d & (d - 1))) return 2;               /* the transform needs d = 2^n */
+    const i64 rows = B * H * N, nblk = (N + 31) / 32;
+    float *y = (float *)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)d * sizeof(float));
+    if (!y) return 3;
+    for (i64 r = 0; r < rows; ++r) {
+        for (i64 c = 0; c < d; ++c) y[r * d + c] = signs ? signs[c] * x[r * d + c] : x[r * d + c];
+        if (signs) fwht_f32(y + r * d, d);
+    }
+    const i64 nsc = B * H * (layout == 0 ? nblk : d);
+    float *amax = (float *)calloc((size_t)(nsc > 0 ? nsc : 1), sizeof(float));
+    if (!amax) { free(y); return 3; }
+    for (i64 bh = 0; bh < B * H; ++bh)
+        for (i64 i = 0; i < N; ++i)
+            for (i64 c = 0; c < d; ++c) {
+                const float a = fabsf(y[(bh * N + i) * d + c]);
+                const i64 g = layout == 0 ? bh * nblk + i / 32 : bh * d + c;
+                if (a > amax[g]) amax[g] = a;
+            }
+    if (whole) {
+        float t = 0.0f;
+        for (i64 g = 0; g < nsc; ++g) if (amax[g] > t) t = amax[g];
+        for (i64 g = 0; g < nsc; ++g) amax[g] = t;
+    }
+    for (i64 g = 0; g < nsc; ++g) scales[g] = (float)ldexp(1.0, scale_exponent(amax[g]));
+    for (i64 bh = 0; bh < B * H; ++bh)
+        for (i64 i = 0; i < N; ++i)
+            for (i64 c = 0; c < d; ++c) {
+                const i64 g = layout == 0 ? bh * nblk + i / 32 : bh * d + c;
+                const float inv = (float)ldexp(1.0, -scale_exponent(amax[g]));
+                codes[(bh * N + i) * d + c] = (unsigned char)orc_e4m3_encode(y[(bh * N + i) * d + c] * inv);
+            }
+    free(amax);
+    free(y);
     return 0;
 }

@@ -675,4 +675,106 @@ def pin_pcast_underflow_claims():
         assert abs(mse["r256"] - mse["f256"]) < 0.05 * mse["f256"], (delta, mse)
 
 
+
+# ---------------------------------------------------------------------------
+# FP8 quantisation with incoherent processing ([MM] "FA3: Mecanica de la
+# tolva", item 3): random-sign Hadamard rotation, power-of-two group scales,
+# E4M3 codes.
+# ---------------------------------------------------------------------------
+
+def _sylvester(d):
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    return h
+
+
+def _min_exponent(amax):
+    """Brute force: the smallest e >= -126 with amax <= 448 * 2^e (exact in fp64)."""
+    if amax == 0:
+        return -126
+    e = -126
+    while float(amax) > 448.0 * 2.0 ** e:
+        e += 1
+    return e
+
+
+def pin_quant_hadamard_matrix():
+    """Sparse small-integer rows: every rotated entry is an integer of size <= 16,
+    which E4M3 holds exactly at any power-of-two scale, so the dequantised
+    codes must equal H_d (s o x) computed with the explicit Sylvester matrix."""
+    g = np.random.default_rng(21)
+    for d in (64, 128):
+        Hm = _sylvester(d)
+        x = np.zeros((1, 2, 40, d), np.float32)
+        for r in range(80):
+            idx = g.choice(d, size=3, replace=False)
+            x.reshape(80, d)[r, idx] = g.choice([-2.0, -1.0, 1.0, 2.0, 3.0], size=3)
+        s = np.where(g.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+        codes, sc = oracle.quant_e4m3(x, signs=s)
+        got = oracle.dequant_e4m3(codes, sc).astype(np.float64)
+        want = (x.astype(np.float64) * s) @ Hm.T
+        assert np.abs(want).max() <= 16
+        assert np.array_equal(got, want), d
+        # H^T H = d I: dot products scale by exactly d
+        assert np.allclose(got[0, 0] @ got[0, 1].T, d * (x[0, 0].astype(np.float64) @ x[0, 1].T))
+
+
+def pin_quant_scale_minimal():
+    """Each 32-row block's scale is 2^e with e the brute-force minimal exponent."""
+    g = np.random.default_rng(22)
+    N, d = 32 * 12 + 7, 64
+    x = g.standard_normal((1, 1, N, d)).astype(np.float32)
+    mags = [0.0, 2.0 ** -140, 2.0 ** -118, 1e-9, 0.5, 1.0, 1.75, 1.7500001, 448.0, 449.0,
+            3.0e5, 2.0 ** 100, 7.0 * 2.0 ** 40]
+    for t, m in enumerate(mags):
+        blk = x[0, 0, 32 * t:32 * t + 32]
+        if m == 0.0:
+            blk[:] = 0.0
+        else:
+            blk *= np.float32(m) / np.abs(blk).max()
+            blk[0, 0] = np.float32(m)          # amax exactly m (as float32)
+    codes, sc = oracle.quant_e4m3(x)
+    for t in range(sc.shape[2]):
+        amax = float(np.abs(x[0, 0, 32 * t:32 * t + 32]).max())
+        assert sc[0, 0, t] == np.float32(2.0 ** _min_exponent(amax)), (t, amax, sc[0, 0, t])
+        assert amax <= 448.0 * float(sc[0, 0, t])
+
+
+def pin_quant_codes_vs_torch():
+    """Codes equal torch's float8_e4m3fn conversion of x / scale, and the round
+    trip stays within half an E4M3 step."""
+    g = np.random.default_rng(23)
+    x = (g.standard_normal((2, 3, 100, 64)) * np.exp(g.normal(0, 3, (2, 3, 100, 1)))).astype(np.float32)
+    codes, sc = oracle.quant_e4m3(x)
+    srow = np.repeat(sc, 32, axis=2)[:, :, :100, None]
+    ref = torch.from_numpy((x / srow).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    deq = oracle.dequant_e4m3(codes, sc).astype(np.float64)
+    y = x.astype(np.float64) / srow
+    bound = np.where(np.abs(y) >= 2.0 ** -6, 2.0 ** -4 * np.abs(y), 2.0 ** -10) * srow
+    assert np.all(np.abs(deq - x) <= bound + 0.0)
+
+
+def pin_quant_group_layouts():
+    """Channel groups, whole-tensor groups and a ragged last row block."""
+    g = np.random.default_rng(24)
+    B, H, N, d = 2, 2, 70, 64
+    x = g.standard_normal((B, H, N, d)).astype(np.float32)
+    x[1, 0, :, 5] *= 1000.0
+    x[0, 1, 64:, :] *= 1e-3
+    _, sc = oracle.quant_e4m3(x, layout="channels")
+    assert sc.shape == (B, H, d)
+    for b in range(B):
+        for h in range(H):
+            for c in range(d):
+                assert sc[b, h, c] == np.float32(2.0 ** _min_exponent(float(np.abs(x[b, h, :, c]).max())))
+    _, sc = oracle.quant_e4m3(x, layout="rows32")
+    assert sc.shape == (B, H, 3)
+    assert sc[0, 1, 2] == np.float32(2.0 ** _min_exponent(float(np.abs(x[0, 1, 64:]).max())))
+    for lay in ("rows32", "channels"):
+        _, sc = oracle.quant_e4m3(x, layout=lay, whole=True)
+        assert np.all(sc == np.float32(2.0 ** _min_exponent(float(np.abs(x).max())))), lay
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

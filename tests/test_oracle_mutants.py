@@ -43,6 +43,12 @@ MUTANTS = [
      "dvb[j * d + c] += dp[j] * (double)doi[c];", 0),
     ("bwd_dq_uses_v", "dqi[c] += J->scale * ds * (double)kj[c];",
      "dqi[c] += J->scale * ds * (double)(vb + j * d)[c];", 0),
+    ("fwht_difference_sign", "y[j + h] = a - b;", "y[j + h] = b - a;", 0),
+    ("fwht_last_stage_dropped", "for (i64 h = 1; h < d; h *= 2)", "for (i64 h = 1; h < d / 2; h *= 2)", 0),
+    ("rotation_signs_ignored", "signs ? signs[c] * x[r * d + c] : x[r * d + c]", "x[r * d + c]", 0),
+    ("scale_exponent_one_low", "(f <= 0.875) ? E2 - 9 : E2 - 8", "(f <= 0.875) ? E2 - 9 : E2 - 9", 0),
+    ("row_block_of_31", "bh * nblk + i / 32 : bh * d + c;", "bh * nblk + i / 31 : bh * d + c;", 0),
+    ("whole_tensor_ignored", "if (whole) {", "if (0) {", 0),
     ("bwd_gqa_one_head", "for (i64 h = hk * g; h < (hk + 1) * g; ++h) {",
      "for (i64 h = hk * g; h < hk * g + 1; ++h) {", 0),
 ]
