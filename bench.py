@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd attn TFLOP/s & % MFMA peak (N=23.4k causal); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 (E4M3) MFMA
 PREFILL_KERNEL = "exact_io_aware_08_amd/csrc/fa_fwd_mfma.hip"
 DECODE_KERNEL = "exact_io_aware_08_amd/csrc/fa_decode.hip"
 
@@ -293,6 +294,30 @@ def main():
                                          "algorithmic_flop": fb,
                                          "note": "dQ, dK, dV from the forward's O and LSE; D, dQ and dK/dV kernels"}
         del g3, ws3, dq3, dk3, dv3
+        # FP8 forward on the trading-day prefill: q, k rotated (random-sign
+        # Hadamard) and quantised per 32-row block, v per column; bf16 output
+        sg = torch.where(torch.rand(d, generator=torch.Generator().manual_seed(0)) < 0.5, -1.0, 1.0)
+        sg = sg.to(torch.float32).to(dev)
+        mq = _timed(lambda i: fa.quant_e4m3(q3, sg), 20, 5, torch)
+        q8, qs8 = fa.quant_e4m3(q3, sg)
+        k8, ks8 = fa.quant_e4m3(k3, sg)
+        mv = _timed(lambda i: fa.quant_e4m3(v3, None, "channels"), 20, 5, torch)
+        v8, vs8 = fa.quant_e4m3(v3, None, "channels")
+        o8 = torch.empty_like(q3)
+        sc8 = float(np.float32(np.float32(c3["scale"]) / d))
+        ms8 = _timed(lambda i: fa.fwd_fp8(q8, k8, v8, qs8, ks8, vs8, causal=True, scale=sc8,
+                                          p_scale=256.0, out=o8, lse=l3), 50, 50, torch)
+        tf8 = flops / (ms8 * 1e-3) / 1e12
+        qbytes = B * H * N * d * (2 + 1) + B * H * ((N + 31) // 32) * 4
+        extra["trading_day_fp8"] = {
+            "ms_per_call": round(ms8, 4), "tflops": round(tf8, 1),
+            "frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+            "speedup_vs_bf16_fwd": round(ms / ms8, 3) if args.only == "all" else None,
+            "quant_rows32_rotated_ms": round(mq, 4),
+            "quant_rows32_rotated_GBps": round(qbytes / (mq * 1e-3) / 1e9, 1),
+            "quant_channels_ms": round(mv, 4),
+            "note": "E4M3 Q, K, V and P (S = 256), running max per 64-key tile; bf16 O"}
+        del q8, k8, v8, o8
         # P-cast on the attention-sink workload: flush counters and time per run
         c5 = fagen.CONFIGS[5]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]

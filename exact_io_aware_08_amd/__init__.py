@@ -213,6 +213,69 @@ def cast_e4m3(x, stream=None):
     return codes, back
 
 
+def quant_e4m3(x, signs=None, layout: str = "rows32", whole: bool = False, codes=None,
+               scales=None, stream=None):
+    """E4M3 codes of x [B,H,N,d] and their power-of-two scales.
+
+    signs: None or a GPU fp32 tensor [d] of +-1 (random-sign Hadamard rotation).
+    layout "rows32": scales [B,H,ceil(N/32)]; "channels": scales [B,H,d].
+    whole=True: one scale for the whole tensor, repeated in that layout."""
+    _check_tensor("x", x, 4)
+    B, H, N, d = x.shape
+    lay = {"rows32": 0, "channels": 1}[layout]
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (N + 31) // 32 if lay == 0 else d), dtype=torch.float32,
+                             device=x.device)
+    if signs is not None and (signs.device != x.device or signs.dtype != torch.float32
+                              or signs.numel() != d or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous fp32 tensor of d values on x's device")
+    st = load().fa_quant_e4m3(x.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                              signs.data_ptr() if signs is not None else None, B, H, N, d,
+                              _DT[x.dtype], lay, int(bool(whole)), _stream_ptr(stream))
+    check(st, "fa_quant_e4m3")
+    return codes, scales
+
+
+def fp8_kv_tile() -> int:
+    return load().fa_fp8_kv_tile()
+
+
+def fwd_fp8(q, k, v, q_scales, k_scales, v_scales, causal: bool = False,
+            scale: float | None = None, p_scale: float = 256.0, kv_reverse: bool = False,
+            out_dtype=torch.bfloat16, out=None, lse=None, stream=None):
+    """FP8 forward over E4M3 codes (uint8 tensors [B,H,Nq,d], [B,Hkv,Nk,d]) with
+    the scales of quant_e4m3 (q, k: "rows32"; v: "channels").  scale defaults
+    to 1/sqrt(d); divide it by d when q and k were rotated."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4 \
+                or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous uint8 GPU tensor [B, heads, seq, d]")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q, k, v shapes disagree")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    want = {"q_scales": (q_scales, (B, H, (Nq + 31) // 32)),
+            "k_scales": (k_scales, (B, Hkv, (Nk + 31) // 32)),
+            "v_scales": (v_scales, (B, Hkv, d))}
+    for n, (t, shp) in want.items():
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{n} must be a contiguous fp32 tensor of shape {shp} on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = load().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scales.data_ptr(),
+                           k_scales.data_ptr(), v_scales.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), float(p_scale),
+                           int(bool(kv_reverse)), _DT[o.dtype], _stream_ptr(stream))
+    check(st, "fa_fwd_fp8")
+    return o, lse
+
+
 def kv_tile(dtype: torch.dtype, d: int, pcast: bool = False) -> int:
     return load().fa_kv_tile(_DT[dtype], d, int(bool(pcast)))
 

@@ -40,6 +40,10 @@ SIGNATURES = {
                              _i, _i, _vp, _sz, _vp]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                     _i, _vp, _sz, _vp]),
+    "fa_quant_e4m3": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "fa_fp8_kv_tile": (_i, []),
+    "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f,
+                        _i, _i, _vp]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_version": (_i, []),
 }

@@ -299,6 +299,54 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
     return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_quant_e4m3(const void *x, uint8_t *codes, float *scales, const float *signs, int B,
+                        int H, int N, int d, fa_dtype dtype, int layout, int whole, void *stream)
+{
+    if (B < 0 || H < 1 || N < 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((layout != 0 && layout != 1) || (whole != 0 && whole != 1)) return FA_ERR_ARG;
+    if ((long long)N * d > kMaxSlice || (long long)B * H > 65535) return FA_ERR_SHAPE;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!x || !codes || !scales) return FA_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) ||
+        (reinterpret_cast<uintptr_t>(signs) & 3u))
+        return FA_ERR_ALIGN;
+    fa_status s = device_status();
+    if (s != FA_OK) return s;
+    fa::QuantProblem p{x, codes, scales, signs, B * H, N, d, (int)dtype, layout, whole};
+    return hip_status(fa::launch_quant(p, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fp8_kv_tile(void) { return fa::fwd_fp8_kv_tile(); }
+
+fa_status fa_fwd_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v, const float *q_scales,
+                     const float *k_scales, const float *v_scales, void *o, float *lse, int B, int H,
+                     int Hkv, int Nq, int Nk, int d, int causal, float scale, float p_scale,
+                     int kv_reverse, fa_dtype o_dtype, void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale);
+    if (s != FA_OK) return s;
+    if ((s = check_fwd_ptrs(q, k, v, o, lse, B, Nq, Nk)) != FA_OK) return s;
+    const bool need_q = B > 0 && Nq > 0, need_kv = B > 0 && Nk > 0;
+    if ((need_q && !q_scales) || (need_kv && (!k_scales || !v_scales))) return FA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(q_scales) & 3u) || (reinterpret_cast<uintptr_t>(k_scales) & 3u) ||
+        !aligned16(v_scales))
+        return FA_ERR_ALIGN;
+    // S: a power of two in [1, 256], so S * p <= 256 < 448 and S divides out exactly
+    int e2 = 0;
+    if (!(std::isfinite(p_scale) && p_scale >= 1.f && p_scale <= 256.f) ||
+        std::frexp(p_scale, &e2) != 0.5f)
+        return FA_ERR_SCALE;
+    if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((causal != 0 && causal != 1) || (kv_reverse != 0 && kv_reverse != 1)) return FA_ERR_ARG;
+    if (!need_q) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::Fp8Problem p{q, k, v, q_scales, k_scales, v_scales, o, lse, B, H, Hkv, Nq, Nk, d,
+                     causal, scale, p_scale, kv_reverse, o_dtype == FA_F32 ? 0 : 2};
+    return hip_status(fa::launch_fwd_fp8(p, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n, void *stream)
 {
     if (n == 0) return FA_OK;

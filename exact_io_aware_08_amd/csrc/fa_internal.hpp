@@ -55,6 +55,30 @@ struct BwdProblem {
     int dtype;
 };
 
+// E4M3 quantisation of one [BH, N, d] tensor.  dtype: 0 = fp32, 1 = fp16,
+// 2 = bf16.  layout 0: scales [BH, ceil(N/32)]; 1: scales [BH, d].
+struct QuantProblem {
+    const void *x;
+    uint8_t *codes;
+    float *scales;
+    const float *signs;  // nullable: no rotation
+    int BH, N, d;
+    int dtype, layout, whole;
+};
+
+// FP8 forward: E4M3 codes with fp32 scales.  o_dtype: 0 = fp32, 2 = bf16.
+struct Fp8Problem {
+    const uint8_t *q, *k, *v;
+    const float *q_scales, *k_scales, *v_scales;
+    void *o;
+    float *lse;  // nullable
+    int B, H, Hkv, Nq, Nk, d;
+    int causal;
+    float scale, p_scale;
+    int kv_reverse;
+    int o_dtype;
+};
+
 // Tile constants shared by the launchers and fa_kv_tile().
 constexpr int kFwdQTile = 128;     // fewest queries per forward workgroup (grid-size bound)
 constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
@@ -66,6 +90,9 @@ hipError_t launch_fwd_mfma(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdProblem &p, hipStream_t stream);
 hipError_t launch_decode(const DecodeProblem &p, hipStream_t stream);
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
+hipError_t launch_quant(const QuantProblem &p, hipStream_t stream);
+int fwd_fp8_kv_tile();        // keys per KV tile of the FP8 kernel (the P-cast tile)
+hipError_t launch_fwd_fp8(const Fp8Problem &p, hipStream_t stream);
 hipError_t launch_cast_e4m3(const float *x, uint8_t *codes, float *back, size_t n,
                             hipStream_t stream);
 

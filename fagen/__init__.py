@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS", "stream_key", "uniform", "normal", "to_storage", "iid_normal",
-    "ar1_series", "sink_inputs", "make_inputs", "sample_rows",
+    "ar1_series", "sink_inputs", "make_inputs", "sample_rows", "outlier_normal", "random_signs",
 ]
 
 _M64 = (1 << 64) - 1
@@ -42,7 +42,7 @@ _C2 = 0x94D049BB133111EB
 
 # Tensor ids used as stream tags.
 T_Q, T_K, T_V = 1, 2, 3
-_KIND_MAIN, _KIND_AR, _KIND_NOISE, _KIND_ROWS = 0, 1, 2, 3
+_KIND_MAIN, _KIND_AR, _KIND_NOISE, _KIND_ROWS, _KIND_OUTLIER, _KIND_SIGNS = 0, 1, 2, 3, 4, 5
 
 _CHUNK = 1 << 22  # elements generated per vectorised step (bounds temporaries)
 
@@ -159,6 +159,24 @@ def sink_inputs(seed: int, B: int, H: int, N: int, d: int, delta: float,
     q[..., 0] = 1.0
     k[:, :, :n_sink, 0] += delta * math.sqrt(d)
     return to_storage(q, "f32"), to_storage(k, "f32"), to_storage(v, "f32")
+
+
+def outlier_normal(seed: int, tensor: int, shape, dtype: str, frac: float = 1e-3,
+                   mag: float = 10.0) -> np.ndarray:
+    """iid N(0,1) entries, each independently (probability frac) multiplied by
+    mag: rare large coordinates, the outliers that spoil naive FP8 attention
+    (marketmaker.cc blog, "FA3: Mecanica de la tolva", item 3)."""
+    n = int(np.prod(shape))
+    x = normal(stream_key(seed, tensor, _KIND_MAIN), n)
+    u = uniform(stream_key(seed, tensor, _KIND_OUTLIER), np.arange(n, dtype=np.int64))
+    x = np.where(u < frac, mag * x, x)
+    return to_storage(x, dtype).reshape(shape)
+
+
+def random_signs(seed: int, d: int) -> np.ndarray:
+    """d random signs (+1.0 / -1.0, fp32) for the random rotation."""
+    u = uniform(stream_key(seed, 0, _KIND_SIGNS), np.arange(d, dtype=np.int64))
+    return np.where(u < 0.5, -1.0, 1.0).astype(np.float32)
 
 
 # Workload table.  'scale' is the fp32 value of 1/sqrt(d).

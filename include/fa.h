@@ -204,6 +204,58 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                  size_t workspace_bytes, void *stream);
 
 /*
+ * E4M3 quantisation for the FP8 forward, with optional incoherent processing
+ * (marketmaker.cc flash-attention post, "FA3: Mecanica de la tolva", item 3:
+ * rotate at random before block-wise quantisation, so outliers spread over
+ * all coordinates).
+ *   y     = H_d (s o x) if signs != NULL, else x.  H_d: Sylvester-Hadamard
+ *           matrix (entries +-1, H_d^T H_d = d I), applied by the fast
+ *           transform in fp32 in stages h = 1, 2, ..., d/2, each replacing
+ *           (y_j, y_{j+h}) (j mod 2h < h) by (y_j + y_{j+h}, y_j - y_{j+h}).
+ *           Rotating q and k with the same signs multiplies q.k by d exactly:
+ *           pass scale / d to fa_fwd_fp8.
+ *   group = layout 0: 32 consecutive rows of one (b, h) -> scales [B,H,ceil(N/32)];
+ *           layout 1: one column of one (b, h)          -> scales [B,H,d];
+ *           whole = 1: one group for the whole tensor, its scale repeated in
+ *           every slot of the layout.
+ *   scale = 2^e, e the smallest integer >= -126 with max|y| over the group
+ *           <= 448 * 2^e (448: the largest finite E4M3 value).
+ *   code  = E4M3_RNE(y * 2^-e) (OCP E4M3FN); the value is decode(code) * 2^e.
+ *   x: device [B,H,N,d] in dtype (FA_F32 / FA_F16 / FA_BF16), 16-byte aligned;
+ *   codes: device [B,H,N,d] bytes, 16-byte aligned; scales: device fp32 as
+ *   above (also used as scratch by layout 1 and whole = 1; contents on entry
+ *   do not matter); signs: NULL or device fp32 [d] of +1/-1.  d: 64 or 128;
+ *   B*H <= 65535.  Inputs must be finite.
+ */
+fa_status fa_quant_e4m3(const void *x, uint8_t *codes, float *scales, const float *signs, int B,
+                        int H, int N, int d, fa_dtype dtype, int layout, int whole, void *stream);
+
+/*
+ * FP8 forward (prefill): attention over dequantised E4M3 operands with the P
+ * cast of gist.science "Resumen Tecnico: Precision de P-Cast en la Atencion
+ * FP8" ("Planteamiento del Problema", "Optimizacion 1"), on the FP8 matrix
+ * cores ("FA3: Mecanica de la tolva", item 3).  With qh, kh, vh the
+ * dequantised values (code value times its group scale) the result is, per
+ * query row, in KV tiles of fa_fp8_kv_tile() keys taken forward (or in
+ * reverse if kv_reverse):
+ *   s_j = scale * qh.kh_j;  m' = max(m, max_j s_j);  p_j = exp(s_j - m');
+ *   l = e^(m - m') l + sum_j p_j;  acc = e^(m - m') acc + sum_j E4M3(p_scale p_j) vh_j;
+ *   O = acc / (p_scale l),  LSE = m + ln l.
+ *   q: [B,H,Nq,d] codes, q_scales [B,H,ceil(Nq/32)] (fa_quant_e4m3 layout 0);
+ *   k: [B,Hkv,Nk,d] codes, k_scales [B,Hkv,ceil(Nk/32)] (layout 0);
+ *   v: [B,Hkv,Nk,d] codes, v_scales [B,Hkv,d] (layout 1, 16-byte aligned).
+ *   Scales are expected to be powers of two (as fa_quant_e4m3 writes them);
+ *   the product q_scale * k_scale * scale is formed in fp32.
+ *   o: [B,H,Nq,d] in o_dtype (FA_BF16 or FA_F32); lse: nullable [B,H,Nq].
+ *   p_scale: a power of two in [1, 256].  Causal convention as fa_fwd.
+ */
+int fa_fp8_kv_tile(void);
+fa_status fa_fwd_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v, const float *q_scales,
+                     const float *k_scales, const float *v_scales, void *o, float *lse, int B, int H,
+                     int Hkv, int Nq, int Nk, int d, int causal, float scale, float p_scale,
+                     int kv_reverse, fa_dtype o_dtype, void *stream);
+
+/*
  * The device E4M3 round trip that fa_fwd_pcast applies to p_scale * P, on n
  * fp32 values: codes[i] = E4M3_RNE(x[i]) (OCP E4M3FN bit pattern),
  * back[i] = the value of that code.  x, codes, back are device pointers

@@ -19,7 +19,8 @@ import numpy as np
 def pcast_bound(a_rows: np.ndarray, v_rows: np.ndarray, S: float, slack: float = 2e-5):
     """a_rows: [R, Nk] exact weights; v_rows: [R, Nk, d] (or [Nk, d] shared).
     Returns the per-element bound [R, d]."""
-    p = a_rows / a_rows.max(axis=1, keepdims=True)
+    mx = a_rows.max(axis=1, keepdims=True)
+    p = np.divide(a_rows, mx, out=np.zeros_like(a_rows, dtype=np.float64), where=mx > 0)
     sp = S * p
     with np.errstate(divide="ignore"):
         r = np.where(sp >= 2.0 ** -6, 2.0 ** -4, np.minimum(1.0, 2.0 ** -10 / sp))

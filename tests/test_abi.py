@@ -204,3 +204,47 @@ def _paged(**kw):
 ])
 def test_decode_paged_validation(kw, expect):
     assert _paged(**kw) == S[expect]
+
+
+def _quant(**kw):
+    a = dict(x=P, codes=P, scales=P, signs=None, B=1, H=2, N=64, d=64, dtype=BF16, layout=0, whole=0)
+    a.update(kw)
+    return fa.load().fa_quant_e4m3(a["x"], a["codes"], a["scales"], a["signs"], a["B"], a["H"],
+                                   a["N"], a["d"], a["dtype"], a["layout"], a["whole"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=96), "FA_ERR_HEADDIM"), (dict(dtype=7), "FA_ERR_DTYPE"), (dict(layout=2), "FA_ERR_ARG"),
+    (dict(whole=2), "FA_ERR_ARG"), (dict(B=-1), "FA_ERR_SHAPE"), (dict(H=0), "FA_ERR_SHAPE"),
+    (dict(B=70000), "FA_ERR_SHAPE"), (dict(x=None), "FA_ERR_NULL"), (dict(scales=None), "FA_ERR_NULL"),
+    (dict(codes=PM), "FA_ERR_ALIGN"), (dict(scales=0x10002), "FA_ERR_ALIGN"),
+    (dict(signs=0x10001), "FA_ERR_ALIGN"), (dict(B=0), "FA_OK"), (dict(N=0, x=None), "FA_OK"),
+])
+def test_quant_validation(kw, expect):
+    assert _quant(**kw) == S[expect]
+
+
+def _fp8(**kw):
+    a = dict(q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=4, Hkv=2, Nq=64, Nk=64, d=64,
+             causal=1, scale=0.125, p_scale=256.0, rev=0, odt=BF16)
+    a.update(kw)
+    return fa.load().fa_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"],
+                                a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                                a["scale"], a["p_scale"], a["rev"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(p_scale=448.0), "FA_ERR_SCALE"), (dict(p_scale=0.5), "FA_ERR_SCALE"),
+    (dict(p_scale=3.0), "FA_ERR_SCALE"), (dict(p_scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(scale=0.0), "FA_ERR_SCALE"), (dict(odt=F16), "FA_ERR_DTYPE"), (dict(causal=2), "FA_ERR_ARG"),
+    (dict(rev=2), "FA_ERR_ARG"), (dict(d=96), "FA_ERR_HEADDIM"), (dict(H=3), "FA_ERR_GQA"),
+    (dict(q=None), "FA_ERR_NULL"), (dict(qs=None), "FA_ERR_NULL"), (dict(vs=None), "FA_ERR_NULL"),
+    (dict(vs=0x10004), "FA_ERR_ALIGN"), (dict(ks=0x10002), "FA_ERR_ALIGN"), (dict(o=PM), "FA_ERR_ALIGN"),
+    (dict(B=0), "FA_OK"), (dict(Nq=0, q=None, o=None, qs=None), "FA_OK"),
+])
+def test_fwd_fp8_validation(kw, expect):
+    assert _fp8(**kw) == S[expect]
+
+
+def test_fp8_kv_tile():
+    assert fa.fp8_kv_tile() == 64
