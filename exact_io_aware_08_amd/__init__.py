@@ -75,7 +75,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 def fwd_pcast(q, k, v, causal: bool = True, scale: float | None = None, p_scale: float = 256.0,
               kv_reverse: bool = True, n_sink: int = 0, counts=None, out=None, lse=None,
               stream=None):
-    """E4M3 P-cast forward (fp32 q, k, v).  Returns (o, lse, counts) where
+    """E4M3 P-cast forward (fp32 or bf16 q, k, v; bf16 is widened exactly on
+    load).  Returns (o, lse, counts) where
     counts (int64 device tensor of 4) holds [non-sink casts, non-sink flushes,
     casts outside the sink tiles, flushes outside the sink tiles]."""
     B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)

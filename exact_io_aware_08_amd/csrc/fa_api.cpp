@@ -150,7 +150,7 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
     if (s != FA_OK) return s;
     if ((s = check_fwd_ptrs(q, k, v, o, lse, B, Nq, Nk)) != FA_OK) return s;
     if (counts && (reinterpret_cast<uintptr_t>(counts) & 7u)) return FA_ERR_ALIGN;
-    if (dtype != FA_F32) return FA_ERR_DTYPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
     if (!(std::isfinite(p_scale) && p_scale > 0.f && p_scale <= 448.f)) return FA_ERR_SCALE;
     if ((causal != 0 && causal != 1) || (kv_reverse != 0 && kv_reverse != 1) || n_sink < 0)
         return FA_ERR_ARG;
@@ -168,7 +168,7 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
 int fa_kv_tile(fa_dtype dtype, int d, int pcast)
 {
     if (d != 64 && d != 128) return -1;
-    if (dtype == FA_F32) return fa::fwd_f32_kv_tile(d);
+    if (dtype == FA_F32 || (pcast && dtype == FA_BF16)) return fa::fwd_f32_kv_tile(d);
     if (pcast) return -1;
     if (dtype == FA_F16 || dtype == FA_BF16) return fa::fwd_mfma_kv_tile(d, 1, 1, 1LL << 30);
     return -1;

@@ -44,10 +44,34 @@ __device__ __forceinline__ unsigned wave_sum_u32(unsigned x)
     return x;
 }
 
-template <int D, bool CAUSAL, bool PCAST>
+// Input elements widen exactly to fp32 on load (TI = float or __bf16, the
+// latter for the P-cast path on bf16 operands); O is written in TI.
+template <typename TI> struct Wide;
+template <> struct Wide<float> {
+    static constexpr int PER = 4;  // elements per 16-byte load
+    static __device__ __forceinline__ void get(const float *p, float (&x)[4])
+    {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(p);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+};
+template <> struct Wide<__bf16> {
+    static constexpr int PER = 8;
+    static __device__ __forceinline__ void get(const __bf16 *p, float (&x)[8])
+    {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // bf16 -> fp32 is a 16-bit shift, exact
+            x[2 * i] = __uint_as_float(v[i] << 16);
+            x[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+        }
+    }
+};
+
+template <typename TI, int D, bool CAUSAL, bool PCAST>
 __global__ void __launch_bounds__(256)
-fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
-               const float *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE,
+fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
+               const TI *__restrict__ V, TI *__restrict__ O, float *__restrict__ LSE,
                int H, int Hkv, int Nq, int Nk, int n_bh, int n_qtiles, float scale,
                float scale_log2, float p_scale, int kv_reverse, int n_sink,
                unsigned long long *__restrict__ counts)
@@ -56,7 +80,8 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     constexpr int NKB = BC / 32;          // 32-key blocks per tile
     constexpr int KSTR = D + 1;           // odd stride: column reads hit 32 banks
     constexpr int VSTR = D;
-    constexpr int CPR = D / 4;            // f32x4_t chunks per row
+    constexpr int PER = Wide<TI>::PER;    // elements per 16-byte chunk
+    constexpr int CPR = D / PER;          // chunks per row
     constexpr int CH = BC * CPR / 256;    // chunks per thread per tensor
     static_assert(CH * 256 == BC * CPR, "tile split");
 
@@ -72,10 +97,10 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     const int hk = h / (H / Hkv);
     const size_t qoff = (size_t)bh * Nq * D;
     const size_t kvoff = ((size_t)b * Hkv + hk) * Nk * D;
-    const float *Qb = Q + qoff;
-    const float *Kb = K + kvoff;
-    const float *Vb = V + kvoff;
-    float *Ob = O + qoff;
+    const TI *Qb = Q + qoff;
+    const TI *Kb = K + kvoff;
+    const TI *Vb = V + kvoff;
+    TI *Ob = O + qoff;
 
     const int q0 = qt * BR;
     const int q0w = q0 + w * 32;
@@ -94,12 +119,11 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     float qop[D / 2];
     const int qrow = min(row, Nq - 1);
 #pragma unroll
-    for (int t4 = 0; t4 < D / 8; ++t4) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(Qb + (size_t)qrow * D + (D / 2) * hh + 4 * t4);
-        qop[4 * t4 + 0] = x.x;
-        qop[4 * t4 + 1] = x.y;
-        qop[4 * t4 + 2] = x.z;
-        qop[4 * t4 + 3] = x.w;
+    for (int t = 0; t < D / 2 / PER; ++t) {
+        float x[PER];
+        Wide<TI>::get(Qb + (size_t)qrow * D + (D / 2) * hh + PER * t, x);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) qop[PER * t + e] = x[e];
     }
 
     f32x16_t acc[D / 32];
@@ -109,15 +133,15 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     unsigned cnt[4] = {0u, 0u, 0u, 0u};
 
     // Keys past Nk load row Nk-1 (masked to weight 0).
-    f32x4_t kreg[CH], vreg[CH];
+    float kreg[CH][PER], vreg[CH][PER];
     auto load_tile = [&](int j) {
         const int j0 = j * BC;
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
             const int ci = tid + r * 256;
             const int key = min(j0 + ci / CPR, Nk - 1), cc = ci % CPR;
-            kreg[r] = *reinterpret_cast<const f32x4_t *>(Kb + (size_t)key * D + 4 * cc);
-            vreg[r] = *reinterpret_cast<const f32x4_t *>(Vb + (size_t)key * D + 4 * cc);
+            Wide<TI>::get(Kb + (size_t)key * D + PER * cc, kreg[r]);
+            Wide<TI>::get(Vb + (size_t)key * D + PER * cc, vreg[r]);
         }
     };
     auto store_tile = [&]() {
@@ -125,12 +149,13 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
         for (int r = 0; r < CH; ++r) {
             const int ci = tid + r * 256;
             const int kl = ci / CPR, cc = ci % CPR;
-            float *kp = &Ks[kl * KSTR + 4 * cc];
-            kp[0] = kreg[r].x;
-            kp[1] = kreg[r].y;
-            kp[2] = kreg[r].z;
-            kp[3] = kreg[r].w;
-            *reinterpret_cast<f32x4_t *>(&Vs[kl * VSTR + 4 * cc]) = vreg[r];
+            float *kp = &Ks[kl * KSTR + PER * cc];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) kp[e] = kreg[r][e];
+#pragma unroll
+            for (int e = 0; e < PER; e += 4)
+                *reinterpret_cast<f32x4_t *>(&Vs[kl * VSTR + PER * cc + e]) =
+                    f32x4_t{vreg[r][e], vreg[r][e + 1], vreg[r][e + 2], vreg[r][e + 3]};
         }
     };
 
@@ -236,9 +261,10 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * mb + 8 * i + 4 * hh;
-                const f32x4_t vals = f32x4_t{acc[mb][4 * i] * inv, acc[mb][4 * i + 1] * inv,
-                                             acc[mb][4 * i + 2] * inv, acc[mb][4 * i + 3] * inv};
-                *reinterpret_cast<f32x4_t *>(Ob + (size_t)row * D + d0) = vals;
+                typedef TI t4 __attribute__((ext_vector_type(4)));
+                const t4 vals = t4{static_cast<TI>(acc[mb][4 * i] * inv), static_cast<TI>(acc[mb][4 * i + 1] * inv),
+                                   static_cast<TI>(acc[mb][4 * i + 2] * inv), static_cast<TI>(acc[mb][4 * i + 3] * inv)};
+                *reinterpret_cast<t4 *>(Ob + (size_t)row * D + d0) = vals;
             }
         if (LSE != nullptr && hh == 0)
             LSE[(size_t)bh * Nq + row] = l > 0.f ? m_run * scale + logf(l) : -INFINITY;
@@ -253,15 +279,15 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     }
 }
 
-template <int D, bool CAUSAL, bool PCAST>
+template <typename TI, int D, bool CAUSAL, bool PCAST>
 hipError_t launch_t(const FwdProblem &p, hipStream_t st)
 {
     const int n_qtiles = (p.Nq + BR - 1) / BR;
     const int n_bh = p.B * p.H;
     const dim3 grid((unsigned)n_qtiles * (unsigned)n_bh), block(256);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, PCAST>), grid, block, 0, st,
-                       static_cast<const float *>(p.q), static_cast<const float *>(p.k),
-                       static_cast<const float *>(p.v), static_cast<float *>(p.o), p.lse, p.H,
+    hipLaunchKernelGGL((fwd_f32_kernel<TI, D, CAUSAL, PCAST>), grid, block, 0, st,
+                       static_cast<const TI *>(p.q), static_cast<const TI *>(p.k),
+                       static_cast<const TI *>(p.v), static_cast<TI *>(p.o), p.lse, p.H,
                        p.Hkv, p.Nq, p.Nk, n_bh, n_qtiles, p.scale, p.scale * kLog2e, p.p_scale,
                        p.kv_reverse, p.n_sink, p.counts);
     return hipGetLastError();
@@ -270,9 +296,11 @@ hipError_t launch_t(const FwdProblem &p, hipStream_t st)
 template <int D>
 hipError_t launch_d(const FwdProblem &p, hipStream_t st)
 {
+    if (p.pcast && p.dtype == 2)  // P-cast on bf16 operands
+        return p.causal ? launch_t<__bf16, D, true, true>(p, st) : launch_t<__bf16, D, false, true>(p, st);
     if (p.pcast)
-        return p.causal ? launch_t<D, true, true>(p, st) : launch_t<D, false, true>(p, st);
-    return p.causal ? launch_t<D, true, false>(p, st) : launch_t<D, false, false>(p, st);
+        return p.causal ? launch_t<float, D, true, true>(p, st) : launch_t<float, D, false, true>(p, st);
+    return p.causal ? launch_t<float, D, true, false>(p, st) : launch_t<float, D, false, false>(p, st);
 }
 
 __global__ void cast_e4m3_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,

@@ -92,8 +92,10 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * "Optimizacion 2"): per KV tile, P = exp(s - m) relative to the RUNNING max
  * m, then P~ = E4M3_RNE(p_scale * P) (OCP E4M3FN), O accumulates P~ V in
  * fp32, the running sum l uses the uncast P, and the epilogue divides by
- * p_scale * l.  Q, K, V stay fp32 (section "Contribuciones Clave", item 4).
- *   dtype      : FA_F32 only.
+ * p_scale * l.  The page keeps Q, K, V in fp32 (section "Contribuciones
+ * Clave", item 4); bf16 operands are also accepted and are widened exactly
+ * to fp32 on load, so the arithmetic after the load is the same.
+ *   dtype      : FA_F32 or FA_BF16 (q, k, v and o all in that type).
  *   p_scale    : the static scale S (256 recommended); finite, > 0, <= 448.
  *   kv_reverse : 0 = KV tiles in increasing key order, 1 = decreasing
  *                (the sink block last).
@@ -105,7 +107,8 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  *                [2] casts of keys outside the KV tiles that hold a sink key,
  *                [3] of those, values flushed to zero.
  *                Only visible (query, key) pairs with query < Nq count.
- * The KV tile width that fixes the tile boundaries is fa_kv_tile(FA_F32, d, 1).
+ * The KV tile width that fixes the tile boundaries is fa_kv_tile(dtype, d, 1)
+ * (the same for both types).
  */
 fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, float *lse,
                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,

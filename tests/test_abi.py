@@ -89,7 +89,7 @@ def _pcast(**kw):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), "FA_ERR_NULL"), (dict(counts=0x10004), "FA_ERR_ALIGN"),
-    (dict(dtype=BF16), "FA_ERR_DTYPE"), (dict(dtype=F16), "FA_ERR_DTYPE"),
+    (dict(dtype=F16), "FA_ERR_DTYPE"),
     (dict(p_scale=0.0), "FA_ERR_SCALE"), (dict(p_scale=512.0), "FA_ERR_SCALE"),
     (dict(rev=2), "FA_ERR_ARG"), (dict(n_sink=-1), "FA_ERR_ARG"),
     (dict(d=32), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
@@ -140,7 +140,8 @@ def test_kv_tile_and_cast_validation():
     assert fa.kv_tile(__import__("torch").bfloat16, 64) in (32, 64)
     lib = fa.load()
     assert lib.fa_kv_tile(F32, 128, 1) in (32, 64)
-    assert lib.fa_kv_tile(BF16, 64, 1) == -1
+    assert lib.fa_kv_tile(BF16, 64, 1) == lib.fa_kv_tile(F32, 64, 1)
+    assert lib.fa_kv_tile(F16, 64, 1) == -1
     assert lib.fa_kv_tile(F32, 48, 0) == -1
     assert lib.fa_cast_e4m3(None, None, None, 4, None) == S["FA_ERR_NULL"]
     assert lib.fa_cast_e4m3(None, None, None, 0, None) == S["FA_OK"]

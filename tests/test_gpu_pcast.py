@@ -19,7 +19,7 @@ import torch
 import exact_io_aware_08_amd as fa
 import fagen
 import oracle
-from gpu_util import announce, need_gpu
+from gpu_util import announce, need_gpu, to_dev
 from pcast_bounds import pcast_bound
 
 pytestmark = pytest.mark.gpu
@@ -126,3 +126,38 @@ def test_pcast_sink_workload_full_size(delta):
             assert cnt[3] == 0, (delta, cnt)
     if delta in (6.0, 8.0):
         assert mse["fwd1"] > 1.2 * mse["rev256"], mse
+
+
+@pytest.mark.parametrize("S,rev,causal", [(1.0, False, True), (256.0, True, True), (256.0, False, False)])
+def test_pcast_bf16_operands(S, rev, causal):
+    """bf16 Q, K, V (the sink workload rounded to bf16): the kernel widens them
+    exactly, so the emulation runs on the widened values.  O is bf16: each
+    element within its own rounding (2^-8 relative) of the emulation for all
+    but 1% of elements, every element within that plus twice the P-cast bound,
+    counts within 1e-4, LSE within 1e-4."""
+    need_gpu()
+    N, H, d = 600, 2, 64
+    announce(f"fa_fwd_pcast bf16 N={N} H={H} d={d} S={S} reverse={rev} causal={causal}")
+    q, k, v = fagen.sink_inputs(0, 1, H, N, d, 6.0)
+    qb, kb, vb = (fagen.to_storage(x.astype(np.float64), "bf16") for x in (q, k, v))
+    wq, wk, wv = (fagen.storage_to_f32(x, "bf16") for x in (qb, kb, vb))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse, cnt = fa.fwd_pcast(*(to_dev(x, "bf16") for x in (qb, kb, vb)), causal=causal,
+                               scale=scale, p_scale=S, kv_reverse=rev, n_sink=4)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    tile = fa.kv_tile(torch.bfloat16, d, pcast=True)
+    assert tile == fa.kv_tile(torch.float32, d, pcast=True)
+    oe, le, ce = oracle.pcast_emulate(wq, wk, wv, causal, scale, tile, S, rev, 4)
+    cnt = [int(x) for x in cnt.cpu()]
+    for i in range(4):
+        assert abs(cnt[i] - ce[i]) <= 1e-4 * max(ce[0], 1) + 3, (cnt, ce)
+    assert np.abs(lse.cpu().numpy() - le).max() <= 1e-4
+    og = o.float().cpu().numpy().astype(np.float64)
+    err = np.abs(og - oe)
+    rnd = 2.0 ** -8 * np.abs(oe) + 1e-6
+    assert np.mean(err > rnd + 1e-4) <= 0.01
+    for h in range(H):
+        a = np.stack([oracle.attention_probs(wq, wk, causal, scale, 0, h, i) for i in range(N)])
+        bnd = pcast_bound(a, wv[0, h], S)
+        assert np.all(err[0, h] <= rnd[0, h] + 2 * bnd), h
