@@ -72,6 +72,23 @@ def _timed(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def _dist(fn, n, torch):
+    """Per-call durations (ms) from one HIP event pair around each call on the
+    current stream, after the main timed region: median, p10, p90."""
+    import numpy as np
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(st)
+        fn(i)
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"n": n, "median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5)}
+
+
 def _sweep(torch, fa, fagen, to_dev, dev):
     """Sequence-length sweep of [MM] "La medicion" at the op level: the
     trading-model inputs (AR(1) + noise, 12 heads, d = 64, causal, bf16) at
@@ -198,6 +215,8 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic},
         })
+        out.setdefault("timing", {})["prefill_per_call"] = _dist(
+            lambda i: fa.fwd(q3, k3, v3, causal=True, scale=c3["scale"], out=o3, lse=l3), 50, torch)
 
     # ---------------- decode ----------------
     if args.only in ("all", "decode"):
@@ -251,6 +270,9 @@ def main():
             paged[name] = {"us_per_call": round(pus, 2), "keys": kv_keys,
                            "GB/s": round(pbytes / (pus * 1e-6) / 1e9, 1)}
         dec["paged"] = paged
+        out.setdefault("timing", {})["decode_per_call"] = _dist(
+            lambda i: fa.decode(q4, caches[i % 4][0], caches[i % 4][1], scale=c4["scale"],
+                                workspace=ws, out=o4, lse=l4), 200, torch)
         del pcaches
         if args.only == "decode":
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
@@ -304,9 +326,10 @@ def main():
         mv = _timed(lambda i: fa.quant_e4m3(v3, None, "channels"), 20, 5, torch)
         v8, vs8 = fa.quant_e4m3(v3, None, "channels")
         o8 = torch.empty_like(q3)
+        l8 = torch.empty_like(l3)  # its own outputs: o3 and l3 are checked against the oracle below
         sc8 = float(np.float32(np.float32(c3["scale"]) / d))
         ms8 = _timed(lambda i: fa.fwd_fp8(q8, k8, v8, qs8, ks8, vs8, causal=True, scale=sc8,
-                                          p_scale=256.0, out=o8, lse=l3), 50, 50, torch)
+                                          p_scale=256.0, out=o8, lse=l8), 50, 50, torch)
         tf8 = flops / (ms8 * 1e-3) / 1e12
         qbytes = B * H * N * d * (2 + 1) + B * H * ((N + 31) // 32) * 4
         extra["trading_day_fp8"] = {
@@ -317,7 +340,7 @@ def main():
             "quant_rows32_rotated_GBps": round(qbytes / (mq * 1e-3) / 1e9, 1),
             "quant_channels_ms": round(mv, 4),
             "note": "E4M3 Q, K, V and P (S = 256), running max per 64-key tile; bf16 O"}
-        del q8, k8, v8, o8
+        del q8, k8, v8, o8, l8
         # P-cast on the attention-sink workload: flush counters and time per run
         c5 = fagen.CONFIGS[5]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
@@ -380,6 +403,19 @@ def main():
                                          f"N={N} causal prefill ({pairs:.3g} visible pairs, "
                                          f"{cpu_s:.1f} s wall); fp64 correctness oracle, not an "
                                          f"optimised CPU baseline"}
+        # the other workloads in full, on the same oracle (seconds, visible pairs per second)
+        others = {}
+        for ci, causal_i in ((1, False), (2, True), (4, False)):
+            cf = fagen.CONFIGS[ci]
+            xs = [fagen.storage_to_f32(x, cf["dtype"]) for x in fagen.make_inputs(cf, 0)]
+            t0 = time.perf_counter()
+            oracle.attention(*xs, causal_i, float(np.float32(1.0 / math.sqrt(cf["d"]))), nthreads=threads)
+            dt = time.perf_counter() - t0
+            Nq_, Nk_ = cf["Nq"], cf["Nk"]
+            npairs = cf["B"] * cf["H"] * (Nq_ * (Nq_ + 1) / 2 if causal_i else Nq_ * Nk_)
+            others[cf["name"]] = {"seconds": round(dt, 4), "pairs_per_s": round(npairs / dt, 1),
+                                  "gflops_fp64": round(4.0 * cf["d"] * npairs / dt / 1e9, 3)}
+        out["cpu_baseline"]["other_configs"] = others
     if "other_workloads" in out and not args.no_cpu_baseline:
         # the P-cast report against the oracle: closed-form flush fraction
         # F(Delta, S) and MSE against exact attention on sampled rows
