@@ -440,6 +440,34 @@ def main():
                 r["mse_vs_exact_sampled"] = float(np.mean((og - o_ex[0]) ** 2))
                 r["F_closed_form"] = float(oracle.F_closed_form(delta, S, d4))
         out["other_workloads"]["pcast_sink_f32"]["mse_rows"] = "8 seeded rows per head"
+        # the page's own setting: N = 4096, MSE of each cast setting against exact attention
+        N6 = 4096
+        rows6 = np.stack([fagen.sample_rows(2, h, N6, 8) for h in range(H5)])
+        q6n, k6n, v6n = fagen.sink_inputs(0, B5, H5, N6, d5, 0.0)
+        q6d, v6d = to_dev(q6n, "f32"), to_dev(v6n, "f32")
+        study = {}
+        for delta in (6.0, 7.0, 8.0):
+            k6n_d = k6n.copy()
+            k6n_d[:, :, :4, 0] += np.float32(delta * math.sqrt(d5))
+            o_ex, _ = oracle.attention(q6n, k6n_d, v6n, True, c5["scale"], rows=rows6,
+                                       nthreads=oracle.default_threads())
+            k6d = to_dev(k6n_d, "f32")
+            mse = {}
+            for name, (S, rev) in (("fwd_S1", (1.0, False)), ("fwd_S256", (256.0, False)),
+                                   ("fwd_S448", (448.0, False)), ("rev_S256", (256.0, True))):
+                o6, _, _ = fa.fwd_pcast(q6d, k6d, v6d, causal=True, scale=c5["scale"], p_scale=S,
+                                        kv_reverse=rev, n_sink=4)
+                og = o6.cpu().numpy()[0][np.arange(H5)[:, None], rows6]
+                mse[name] = float(np.mean((og - o_ex[0]) ** 2))
+            study[f"delta{delta:g}"] = {
+                "mse": mse,
+                "fwd_S1_over_rev_S256": round(mse["fwd_S1"] / mse["rev_S256"], 3),
+                "fwd_S1_over_fwd_S256": round(mse["fwd_S1"] / mse["fwd_S256"], 3),
+                "fwd_S448_over_fwd_S256": round(mse["fwd_S448"] / mse["fwd_S256"], 3),
+                "rev_S256_over_fwd_S256": round(mse["rev_S256"] / mse["fwd_S256"], 3)}
+            del k6d
+        out["other_workloads"]["pcast_sink_f32"]["n4096_study"] = {
+            "shape": [B5, H5, N6, d5], "rows": "8 seeded rows per head", "by_delta": study}
     print(json.dumps(out))
 
 
