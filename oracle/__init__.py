@@ -203,8 +203,10 @@ def attention_probs(q, k, causal: bool, scale: float, b: int, h: int, i: int) ->
 
 
 def pcast_emulate(q, k, v, causal: bool, scale: float, kv_tile: int, p_scale: float,
-                  reverse: bool, n_sink: int = 0, rows=None, nthreads: int | None = None):
-    """orc_pcast: E4M3 P-cast emulation.
+                  reverse: bool, n_sink: int = 0, rows=None, nthreads: int | None = None,
+                  tile_local: bool = False):
+    """orc_pcast: E4M3 P-cast emulation (tile_local: P relative to each tile's
+    own maximum instead of the running one -- the ablation).
 
     Returns (O, LSE, counts) with counts = [casts, zeros] over keys >= n_sink
     followed by [casts, zeros] over keys outside the KV tiles holding a sink.
@@ -221,7 +223,8 @@ def pcast_emulate(q, k, v, causal: bool, scale: float, kv_tile: int, p_scale: fl
     counts = np.zeros(4, dtype=np.uint64)
     rc = lib.orc_pcast(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, H, Hkv, Nq, Nk, d,
                        int(bool(causal)), float(np.float32(scale)), int(kv_tile),
-                       float(np.float32(p_scale)), int(bool(reverse)), int(n_sink),
+                       float(np.float32(p_scale)), int(bool(reverse)) | (int(bool(tile_local)) << 1),
+                       int(n_sink),
                        None if r is None else _ptr(r, _ip), R, _ptr(o, _dp), _ptr(lse, _dp),
                        _ptr(counts, _up), nthreads or default_threads())
     if rc != 0:

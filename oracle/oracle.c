@@ -78,6 +78,7 @@ typedef struct {
     float p_scale;
     float scale_f;
     int reverse;
+    int tile_local;    /* ablation: P relative to each tile's own max */
     i64 n_sink;
     /* work distribution */
     i64 n_items;
@@ -224,19 +225,28 @@ static void pcast_row(job_t *J, i64 b, i64 h, i64 i, double *o_row, double *lse_
             s[j - j0] = (float)((double)J->scale_f * dot(qi, kb + j * d, d));
             if (s[j - j0] > mn) mn = s[j - j0];
         }
+        /* The tile-local ablation (FA1's form in [MM] "El algoritmo de atencion
+         * flash"): P relative to this tile's own maximum mt, so its largest
+         * value casts from exactly S; its weight is restored by
+         * beta = exp(mt - mn).  Default: P relative to the running max, beta = 1. */
+        float mt = -INFINITY;
+        for (i64 j = j0; j < j1; ++j)
+            if (s[j - j0] > mt) mt = s[j - j0];
+        const float pref = J->tile_local ? mt : mn;
+        const double beta = J->tile_local ? exp((double)mt - (double)mn) : 1.0;
         const double a = (m == -INFINITY) ? 0.0 : exp((double)m - (double)mn);
         l *= a;
         for (i64 c = 0; c < d; ++c) o_row[c] *= a;
         for (i64 j = j0; j < j1; ++j) {
-            const float p = (float)exp((double)s[j - j0] - (double)mn);
-            l += (double)p;
+            const float p = (float)exp((double)s[j - j0] - (double)pref);
+            l += (double)p * beta;
             const float x = p * J->p_scale;
             const float pt = orc_e4m3_decode(orc_e4m3_encode(x));
             const int flushed = (pt == 0.0f && p > 0.0f);
             if (j >= J->n_sink) { cnt[0] += 1; cnt[1] += flushed; }
             if (j >= sink_end) { cnt[2] += 1; cnt[3] += flushed; }
             const float *vj = vb + j * d;
-            for (i64 c = 0; c < d; ++c) o_row[c] += (double)pt * (double)vj[c];
+            for (i64 c = 0; c < d; ++c) o_row[c] += beta * (double)pt * (double)vj[c];
         }
         m = mn;
     }
@@ -345,7 +355,9 @@ int orc_pcast(const float *q, const float *k, const float *v, i64 B, i64 H, i64 
     J.q = q; J.k = k; J.v = v; J.B = B; J.H = H; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
     J.causal = causal; J.scale = (double)scale; J.scale_f = scale; J.rows = rows;
     J.nrows = nrows; J.o = o; J.lse = lse;
-    J.pcast = 1; J.kv_tile = kv_tile; J.p_scale = p_scale; J.reverse = reverse;
+    /* reverse: bit 0 = KV tiles in reverse order, bit 1 = tile-local max */
+    J.pcast = 1; J.kv_tile = kv_tile; J.p_scale = p_scale; J.reverse = reverse & 1;
+    J.tile_local = (reverse >> 1) & 1;
     J.n_sink = n_sink;
     const int rc = run(&J, nthreads);
     if (counts) for (int c = 0; c < 4; ++c) counts[c] = J.cnt[c];

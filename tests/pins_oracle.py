@@ -539,8 +539,9 @@ ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 # P-cast emulation ([PC] "Planteamiento del Problema", "Optimizacion 1/2")
 # --------------------------------------------------------------------------
 
-def _pcast_python(q, k, v, scale, Bc, S, reverse, n_sink):
-    """Independent tiny implementation; the E4M3 cast is torch's float8_e4m3fn."""
+def _pcast_python(q, k, v, scale, Bc, S, reverse, n_sink, tile_local=False):
+    """Independent tiny implementation; the E4M3 cast is torch's float8_e4m3fn.
+    tile_local: P relative to each tile's own max, weight exp(mt - m_new)."""
     Nq, d = q.shape
     Nk = k.shape[0]
     O = np.zeros((Nq, d))
@@ -559,12 +560,15 @@ def _pcast_python(q, k, v, scale, Bc, S, reverse, n_sink):
                                                                     k[j].astype(np.float64))))
                  for j in js]
             mn = max([m] + s)
+            mt = max(s)
+            ref = mt if tile_local else mn
+            w = math.exp(float(mt) - float(mn)) if tile_local else 1.0
             a = 0.0 if m == -np.inf else math.exp(float(m) - float(mn))
             l *= a
             acc *= a
             for j, sj in zip(js, s):
-                p = np.float32(math.exp(float(sj) - float(mn)))
-                l += float(p)
+                p = np.float32(math.exp(float(sj) - float(ref)))
+                l += float(p) * w
                 x = np.float32(p * np.float32(S))
                 pt = float(torch.tensor([float(x)], dtype=torch.float32)
                            .to(torch.float8_e4m3fn).float()[0])
@@ -575,7 +579,7 @@ def _pcast_python(q, k, v, scale, Bc, S, reverse, n_sink):
                 if j >= sink_end:
                     cnt[2] += 1
                     cnt[3] += fl
-                acc += pt * v[j].astype(np.float64)
+                acc += w * pt * v[j].astype(np.float64)
             m = mn
         O[i] = acc / (S * l)
         L[i] = float(m) + math.log(l)
@@ -591,11 +595,29 @@ def pin_pcast_bruteforce_tiny():
     k[0, 0, :2, 0] += 6.0   # two sink keys
     q[0, 0, :, 0] = 1.0
     for (Bc, S, rev) in ((4, 1.0, False), (4, 256.0, True), (3, 448.0, False), (5, 256.0, False)):
-        o, lse, cnt = oracle.pcast_emulate(q, k, v, True, 0.5, Bc, S, rev, n_sink=2)
-        O, L, c2 = _pcast_python(q[0, 0], k[0, 0], v[0, 0], 0.5, Bc, S, rev, 2)
-        assert np.allclose(o[0, 0], O, rtol=1e-12, atol=1e-12), (Bc, S, rev)
-        assert np.allclose(lse[0, 0], L, rtol=1e-12, atol=1e-12), (Bc, S, rev)
-        assert cnt == c2, (Bc, S, rev, cnt, c2)
+        for tl in (False, True):
+            o, lse, cnt = oracle.pcast_emulate(q, k, v, True, 0.5, Bc, S, rev, n_sink=2, tile_local=tl)
+            O, L, c2 = _pcast_python(q[0, 0], k[0, 0], v[0, 0], 0.5, Bc, S, rev, 2, tile_local=tl)
+            assert np.allclose(o[0, 0], O, rtol=1e-12, atol=1e-12), (Bc, S, rev, tl)
+            assert np.allclose(lse[0, 0], L, rtol=1e-12, atol=1e-12), (Bc, S, rev, tl)
+            assert cnt == c2, (Bc, S, rev, tl, cnt, c2)
+
+
+def pin_pcast_tile_local_ablation():
+    """The tile-local ablation: with one tile covering every key it is the
+    running-max emulation exactly; with many tiles on a strong sink (forward,
+    S = 1) it flushes far fewer non-sink values, since every tile's largest P
+    casts from exactly S instead of from a value shrunk by the sink."""
+    q, k, v = _inputs(1, 2, 2, 200, 200, 16, seed=64)
+    q[..., 0] = 1.0
+    k[:, :, :4, 0] += 8.0 * 4.0
+    a = oracle.pcast_emulate(q, k, v, True, 0.25, 256, 1.0, False, 4)
+    b = oracle.pcast_emulate(q, k, v, True, 0.25, 256, 1.0, False, 4, tile_local=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+    run = oracle.pcast_emulate(q, k, v, True, 0.25, 16, 1.0, False, 4)
+    loc = oracle.pcast_emulate(q, k, v, True, 0.25, 16, 1.0, False, 4, tile_local=True)
+    assert run[2][1] > 0.5 * run[2][0], run[2]           # P-collapse under the running max
+    assert loc[2][3] < 0.1 * max(run[2][3], 1), (run[2], loc[2])
 
 
 def pin_pcast_single_key():

@@ -28,8 +28,12 @@ MUTANTS = [
     ("v_uses_key", "o_row[c] += p * (double)vj[c];", "o_row[c] += p * (double)(kb + j * d)[c];", 0),
     ("pcast_no_rescale", "for (i64 c = 0; c < d; ++c) o_row[c] *= a;", "", 0),
     ("pcast_reverse_ignored", "J->reverse ? (ntiles - 1 - tt) : tt", "tt", 0),
-    ("pcast_sum_of_cast", "l += (double)p;",
-     "l += (double)orc_e4m3_decode(orc_e4m3_encode(p * J->p_scale)) / J->p_scale;", 0),
+    ("pcast_sum_of_cast", "l += (double)p * beta;",
+     "l += (double)orc_e4m3_decode(orc_e4m3_encode(p * J->p_scale)) / J->p_scale * beta;", 0),
+    ("pcast_tile_local_weight_dropped", "const double beta = J->tile_local ? exp((double)mt - (double)mn) : 1.0;",
+     "const double beta = 1.0;", 0),
+    ("pcast_tile_local_uses_running_max", "const float pref = J->tile_local ? mt : mn;",
+     "const float pref = mn;", 0),
     ("pcast_tile_local_max", "float mn = m;", "float mn = -INFINITY;", 0),
     ("pcast_scale_not_divided", "const double den = (double)J->p_scale * l;", "const double den = l;", 0),
     ("e4m3_subnormal_step", "nearbyint(a * 512.0)", "nearbyint(a * 1024.0)", 0),
