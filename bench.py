@@ -453,10 +453,12 @@ def main():
                                        nthreads=oracle.default_threads())
             k6d = to_dev(k6n_d, "f32")
             mse = {}
-            for name, (S, rev) in (("fwd_S1", (1.0, False)), ("fwd_S256", (256.0, False)),
-                                   ("fwd_S448", (448.0, False)), ("rev_S256", (256.0, True))):
+            for name, (S, rev, loc) in (("fwd_S1", (1.0, False, False)), ("fwd_S256", (256.0, False, False)),
+                                        ("fwd_S448", (448.0, False, False)), ("rev_S256", (256.0, True, False)),
+                                        ("fwd_S1_tile_local", (1.0, False, True)),
+                                        ("fwd_S256_tile_local", (256.0, False, True))):
                 o6, _, _ = fa.fwd_pcast(q6d, k6d, v6d, causal=True, scale=c5["scale"], p_scale=S,
-                                        kv_reverse=rev, n_sink=4)
+                                        kv_reverse=rev, n_sink=4, tile_local_max=loc)
                 og = o6.cpu().numpy()[0][np.arange(H5)[:, None], rows6]
                 mse[name] = float(np.mean((og - o_ex[0]) ** 2))
             study[f"delta{delta:g}"] = {
@@ -464,7 +466,9 @@ def main():
                 "fwd_S1_over_rev_S256": round(mse["fwd_S1"] / mse["rev_S256"], 3),
                 "fwd_S1_over_fwd_S256": round(mse["fwd_S1"] / mse["fwd_S256"], 3),
                 "fwd_S448_over_fwd_S256": round(mse["fwd_S448"] / mse["fwd_S256"], 3),
-                "rev_S256_over_fwd_S256": round(mse["rev_S256"] / mse["fwd_S256"], 3)}
+                "rev_S256_over_fwd_S256": round(mse["rev_S256"] / mse["fwd_S256"], 3),
+                "fwd_S1_tile_local_over_fwd_S1": round(mse["fwd_S1_tile_local"] / mse["fwd_S1"], 3),
+                "fwd_S256_tile_local_over_fwd_S256": round(mse["fwd_S256_tile_local"] / mse["fwd_S256"], 3)}
             del k6d
         out["other_workloads"]["pcast_sink_f32"]["n4096_study"] = {
             "shape": [B5, H5, N6, d5], "rows": "8 seeded rows per head", "by_delta": study}

@@ -74,7 +74,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 
 def fwd_pcast(q, k, v, causal: bool = True, scale: float | None = None, p_scale: float = 256.0,
               kv_reverse: bool = True, n_sink: int = 0, counts=None, out=None, lse=None,
-              stream=None):
+              stream=None, tile_local_max: bool = False):
     """E4M3 P-cast forward (fp32 or bf16 q, k, v; bf16 is widened exactly on
     load).  Returns (o, lse, counts) where
     counts (int64 device tensor of 4) holds [non-sink casts, non-sink flushes,
@@ -89,7 +89,8 @@ def fwd_pcast(q, k, v, causal: bool = True, scale: float | None = None, p_scale:
         counts = torch.zeros(4, dtype=torch.int64, device=q.device)
     st = load().fa_fwd_pcast(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), B, H, Hkv, Nq, Nk, d, int(bool(causal)),
-                             float(scale), _DT[q.dtype], float(p_scale), int(bool(kv_reverse)),
+                             float(scale), _DT[q.dtype], float(p_scale),
+                             int(bool(kv_reverse)) | (int(bool(tile_local_max)) << 1),
                              int(n_sink), counts.data_ptr(), _stream_ptr(stream))
     check(st, "fa_fwd_pcast")
     return o, lse, counts

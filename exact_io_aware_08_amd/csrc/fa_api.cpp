@@ -152,8 +152,7 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
     if (counts && (reinterpret_cast<uintptr_t>(counts) & 7u)) return FA_ERR_ALIGN;
     if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
     if (!(std::isfinite(p_scale) && p_scale > 0.f && p_scale <= 448.f)) return FA_ERR_SCALE;
-    if ((causal != 0 && causal != 1) || (kv_reverse != 0 && kv_reverse != 1) || n_sink < 0)
-        return FA_ERR_ARG;
+    if ((causal != 0 && causal != 1) || (kv_reverse & ~3) != 0 || n_sink < 0) return FA_ERR_ARG;
     if (B == 0 || Nq == 0) return FA_OK;
     if ((s = device_status()) != FA_OK) return s;
     fa::FwdProblem p{};

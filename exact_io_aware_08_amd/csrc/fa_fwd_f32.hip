@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(256)
 fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
                const TI *__restrict__ V, TI *__restrict__ O, float *__restrict__ LSE,
                int H, int Hkv, int Nq, int Nk, int n_bh, int n_qtiles, float scale,
-               float scale_log2, float p_scale, int kv_reverse, int n_sink,
+               float scale_log2, float p_scale, int kv_flags, int n_sink,
                unsigned long long *__restrict__ counts)
 {
     constexpr int BC = F32Tile<D>::BC;
@@ -159,6 +159,8 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
         }
     };
 
+    const bool kv_reverse = (kv_flags & 1) != 0;  // bit 0: KV tiles in reverse order
+    const bool tile_local = (kv_flags & 2) != 0;  // bit 1: tile-local max (P-cast ablation)
     auto tile_at = [&](int jj) { return kv_reverse ? (nkt - 1 - jj) : jj; };
     if (nkt > 0) load_tile(tile_at(0));
     for (int jj = 0; jj < nkt; ++jj) {
@@ -200,7 +202,13 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-        const float mneg = -m_use * scale_log2;
+        // P relative to the running max; in the tile-local ablation (P-cast
+        // only) relative to this tile's own max, its weight restored by
+        // beta = exp(m_tile - m_new) after the cast
+        const bool local = PCAST && tile_local;
+        const float m_ref = local ? ((mx == -INFINITY) ? 0.f : mx) : m_use;
+        const float beta = local ? ((mx == -INFINITY) ? 0.f : fast_exp2((m_ref - m_use) * scale_log2)) : 1.f;
+        const float mneg = -m_ref * scale_log2;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -210,7 +218,7 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
                 s[kb][r] = p;
                 rs += p;
             }
-        l_run = l_run * alpha + rs;
+        l_run = l_run * alpha + (local ? rs * beta : rs);
         m_run = m_new;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
@@ -224,8 +232,8 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
                     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * p_scale, p1 * p_scale, 0, false);
                     const float t0 = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
                     const float t1 = __builtin_amdgcn_cvt_f32_fp8(pk, 1);
-                    s[kb][r] = t0;
-                    s[kb][r + 1] = t1;
+                    s[kb][r] = local ? t0 * beta : t0;
+                    s[kb][r + 1] = local ? t1 * beta : t1;
                     const int key0 = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
                     const int key1 = key0 + 1;
                     const unsigned f0 = (t0 == 0.f && p0 > 0.f), f1 = (t1 == 0.f && p1 > 0.f);

@@ -21,7 +21,7 @@ struct FwdProblem {
     // E4M3 P-cast variant (fp32 kernel only)
     int pcast;
     float p_scale;
-    int kv_reverse;
+    int kv_reverse;  // bit 0: reverse KV order; bit 1: tile-local max (ablation)
     int n_sink;
     unsigned long long *counts;  // nullable, 4 entries
 };

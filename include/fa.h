@@ -97,8 +97,12 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * to fp32 on load, so the arithmetic after the load is the same.
  *   dtype      : FA_F32 or FA_BF16 (q, k, v and o all in that type).
  *   p_scale    : the static scale S (256 recommended); finite, > 0, <= 448.
- *   kv_reverse : 0 = KV tiles in increasing key order, 1 = decreasing
- *                (the sink block last).
+ *   kv_reverse : bit 0: 0 = KV tiles in increasing key order, 1 = decreasing
+ *                (the sink block last).  Bit 1 (an ablation, FA1's form in
+ *                marketmaker.cc "El algoritmo de atencion flash"): P is taken
+ *                relative to each tile's own max and its weight restored by
+ *                exp(m_tile - m) after the cast, so every tile's largest P
+ *                casts from exactly p_scale.  Other bits must be 0.
  *   n_sink     : keys [0, n_sink) are sink keys, excluded from counts[0..1].
  *   counts     : NULL, or a device array of 4 uint64 to which the call ADDS
  *                (the caller initialises it):

@@ -91,7 +91,7 @@ def _pcast(**kw):
     (dict(q=None), "FA_ERR_NULL"), (dict(counts=0x10004), "FA_ERR_ALIGN"),
     (dict(dtype=F16), "FA_ERR_DTYPE"),
     (dict(p_scale=0.0), "FA_ERR_SCALE"), (dict(p_scale=512.0), "FA_ERR_SCALE"),
-    (dict(rev=2), "FA_ERR_ARG"), (dict(n_sink=-1), "FA_ERR_ARG"),
+    (dict(rev=4), "FA_ERR_ARG"), (dict(rev=-1), "FA_ERR_ARG"), (dict(n_sink=-1), "FA_ERR_ARG"),
     (dict(d=32), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
 ])
 def test_pcast_validation(kw, expect):

@@ -161,3 +161,34 @@ def test_pcast_bf16_operands(S, rev, causal):
         a = np.stack([oracle.attention_probs(wq, wk, causal, scale, 0, h, i) for i in range(N)])
         bnd = pcast_bound(a, wv[0, h], S)
         assert np.all(err[0, h] <= rnd[0, h] + 2 * bnd), h
+
+
+@pytest.mark.parametrize("d,S,rev", [(64, 1.0, False), (128, 256.0, False), (64, 256.0, True)])
+def test_pcast_tile_local_ablation(d, S, rev):
+    """The tile-local-max ablation against its emulation (same criteria as the
+    running-max runs), and its effect: on a strong sink with forward order it
+    flushes far fewer non-sink values than the running-max form."""
+    need_gpu()
+    N, H = 1000, 2
+    announce(f"fa_fwd_pcast tile-local d={d} S={S} reverse={rev}")
+    q, k, v = fagen.sink_inputs(0, 1, H, N, d, 8.0)
+    tile = fa.kv_tile(torch.float32, d, pcast=True)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    o, lse, cnt = fa.fwd_pcast(dq, dk, dv, causal=True, scale=scale, p_scale=S, kv_reverse=rev,
+                               n_sink=4, tile_local_max=True)
+    _, _, cnt_run = fa.fwd_pcast(dq, dk, dv, causal=True, scale=scale, p_scale=S, kv_reverse=rev,
+                                 n_sink=4)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    cnt, cnt_run = [int(x) for x in cnt.cpu()], [int(x) for x in cnt_run.cpu()]
+    oe, le, ce = oracle.pcast_emulate(q, k, v, True, scale, tile, S, rev, 4, tile_local=True)
+    for i in range(4):
+        assert abs(cnt[i] - ce[i]) <= 1e-4 * max(ce[0], 1) + 3, (cnt, ce)
+    o_ex, _ = oracle.attention(q, k, v, True, scale)
+    mse_g, mse_e = np.mean((o - o_ex) ** 2), np.mean((oe - o_ex) ** 2)
+    assert abs(mse_g - mse_e) <= 0.05 * mse_e, (mse_g, mse_e)
+    assert np.mean(np.abs(o - oe) > 1e-4) <= 0.01
+    assert np.abs(lse - le).max() <= 1e-4
+    if S == 1.0 and not rev:
+        assert cnt[3] < 0.1 * max(cnt_run[3], 1), (cnt, cnt_run)
