@@ -91,21 +91,21 @@ def _dist(fn, n, torch):
 
 def _sweep(torch, fa, fagen, to_dev, dev):
     """Sequence-length sweep of [MM] "La medicion" at the op level: the
-    trading-model inputs (AR(1) + noise, 12 heads, d = 64, causal, bf16) at
-    N = 512, 4,096 and 32,768.  For each N: fa_fwd and fa_fwd + fa_bwd time and
+    trading-model inputs (AR(1) + noise, 12 heads, causal, bf16) at
+    N = 512, 4,096 and 32,768, for head dims 64 and 128.  For each N: fa_fwd and fa_fwd + fa_bwd time and
     the extra device memory each call allocates, against the materialised
     definition (scores, softmax and P V as separate bf16 tensor ops, the
     standard path of [MM] "Por que la atencion esta ligada a la memoria"),
     forward only."""
     res = {"metric": "op cost vs sequence length (fa_fwd / fa_bwd vs materialised attention)",
            "data": "synthetic AR(1) phi=0.9 + N(0,0.1), seed 0", "dtype": "bf16", "rows": []}
-    for N in (512, 4096, 32768):
-        cfg = dict(B=1, H=12, Hkv=12, Nq=N, Nk=N, d=64, dtype="bf16", kind="ar1")
+    for d, N in ((64, 512), (64, 4096), (64, 32768), (128, 512), (128, 4096), (128, 32768)):
+        cfg = dict(B=1, H=12, Hkv=12, Nq=N, Nk=N, d=d, dtype="bf16", kind="ar1")
         qn, kn, vn = fagen.make_inputs(cfg, 0)
         q, k, v = (to_dev(x, "bf16") for x in (qn, kn, vn))
-        scale = 0.125
-        flops = 2.0 * 64 * 12 * N * (N + 1)
-        row = {"N": N, "score_matrix_bytes_bf16": 12 * N * N * 2}
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+        flops = 2.0 * d * 12 * N * (N + 1)
+        row = {"d": d, "N": N, "score_matrix_bytes_bf16": 12 * N * N * 2}
 
         def peak(fn):
             torch.cuda.synchronize()
