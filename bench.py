@@ -302,6 +302,26 @@ def main():
                                        "tflops": round(f2 / (ms2 * 1e-3) / 1e12, 1),
                                        "frac_of_bf16_peak": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                        "shape": [4, 12, 2048, 64], "causal": True}
+        # decode at other shapes: MHA (one query head per KV head, so 15 of the 16
+        # query slots of the MFMA N dimension idle) and a single long sequence
+        # (small B*Hkv, filled by splits); both should still stream the cache
+        for name, (Bx, Hx, Hkvx, Nkx) in (("mha_decode_bf16", (16, 32, 32, 2048)),
+                                          ("single_sequence_decode_bf16", (1, 32, 4, 65536))):
+            cx = dict(B=Bx, H=Hx, Hkv=Hkvx, Nq=1, Nk=Nkx, d=64, dtype="bf16", kind="iid")
+            qxn, kxn, vxn = fagen.make_inputs(cx, 0)
+            qx = to_dev(qxn, "bf16")
+            cachex = [(to_dev(kxn, "bf16"), to_dev(vxn, "bf16"))]
+            for r in range(1, 4):
+                cachex.append((cachex[0][0].clone(), cachex[0][1].clone()))
+            wsx = fa.decode_workspace(Bx, Hx, Hkvx, Nkx, 64, device=dev)
+            usx = 1e3 * _timed(lambda i: fa.decode(qx, cachex[i % 4][0], cachex[i % 4][1], scale=0.125,
+                                                   workspace=wsx), 200, 200, torch)
+            bx = 2 * Bx * Hkvx * Nkx * 64 * 2 + Bx * Hx * 64 * 2 * 2 + Bx * Hx * 4
+            extra[name] = {"B": Bx, "H": Hx, "Hkv": Hkvx, "Nk": Nkx, "d": 64,
+                           "splits": fa.decode_splits(Bx, Hx, Hkvx, Nkx), "us_per_call": round(usx, 2),
+                           "GB/s": round(bx / (usx * 1e-6) / 1e9, 1),
+                           "frac_of_hbm_peak": round(bx / (usx * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            del cachex, qx, wsx
         # backward by recomputation on the trading-day prefill (GPU forward's O, LSE)
         g3 = torch.empty_like(q3).normal_(generator=torch.Generator(device=dev).manual_seed(0))
         ws3 = torch.empty(max(fa.bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8, device=dev)
