@@ -15,7 +15,10 @@
 // "Innovazioni chiave": one fused kernel that writes only O (and the LSE).
 //
 // gfx950 mapping (one workgroup = 4 waves; each wave owns QB blocks of 32
-// query rows of one (b, h); a KV tile has NKB blocks of 32 keys, QB*NKB = 2):
+// query rows of one (b, h); a KV tile has NKB blocks of 32 keys; QB*NKB = 2
+// score blocks per wave at d = 64, one at d = 128, where a 32-key tile keeps
+// the LDS of a workgroup at 48 KB and the registers under 256, so two waves
+// share each SIMD):
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16:
 //    the fp32 result gives lane l the 16 keys {8i + 4(l/32) + r} of query
 //    l%32 per 32x32 block, so a row's max needs one v_permlane32_swap and
@@ -76,7 +79,10 @@ template <> struct Pack2<_Float16> {
 
 // Geometry for head dim D and QB query blocks per wave.
 template <int D, int QB> struct Geo {
-    static constexpr int NKB = 2 / QB;           // 32-key blocks per KV tile
+    static constexpr int NKB = (QB >= 2 || D == 128) ? 1 : 2;  // 32-key blocks per KV tile
+    // (d = 128 with 64-key tiles needed 96 KB of LDS: one workgroup, one wave
+    //  per SIMD, 1.5x slower than two waves with 32-key tiles)
+    static constexpr int NSB = QB * NKB;         // 32x32 score blocks per wave
     static constexpr int BC = 32 * NKB;          // keys per KV tile
     static constexpr int BR = NW * 32 * QB;      // queries per workgroup
     static constexpr int KSTR = D + 8;           // K tile row stride in LDS (elements)
@@ -87,7 +93,6 @@ template <int D, int QB> struct Geo {
     static constexpr int VS = D == 64 ? 96 : 160;
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     static constexpr int KCH = BC * CPR / 256;   // K (and V) chunks per thread per tile
-    static_assert(QB * NKB == 2, "two 32x32 score blocks per wave");
     static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "staging split");
     static_assert(VS >= D && (VS * 2) % 16 == 0, "V row stride");
 };
@@ -134,13 +139,13 @@ __device__ __forceinline__ void store_rows(T *buf, const int (&st)[Geo<D, QB>::K
 // qb * NKB + kb.  Each K operand read serves all QB query blocks.
 template <typename T, int D, int QB>
 __device__ __forceinline__ void scores(const T *Ks, const typename Mma16<T>::v8 (&qop)[QB][D / 16],
-                                       int c, int hh, f32x16_t (&s)[2])
+                                       int c, int hh, f32x16_t (&s)[Geo<D, QB>::NSB])
 {
     using M = Mma16<T>;
     using v8 = typename M::v8;
     using G = Geo<D, QB>;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) s[i] = f32x16_t{};
+    for (int i = 0; i < G::NSB; ++i) s[i] = f32x16_t{};
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
 #pragma unroll
@@ -165,7 +170,7 @@ __device__ __forceinline__ float sum_pair(float x)
 }
 
 template <typename T, int D, int QB, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, QB >= 3 ? 1 : 2)
 fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                 T *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk,
                 int n_bh, int n_qtiles, float scale, float scale_log2)
@@ -174,7 +179,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     using v8 = typename M::v8;
     using P2 = Pack2<T>;
     using G = Geo<D, QB>;
-    constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS;
+    constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS, NSB = G::NSB;
 
     __shared__ __attribute__((aligned(16))) T Kbuf[2][BC * G::KSTR];
     __shared__ __attribute__((aligned(16))) T Vbuf[3][BC * VS];  // tile i in Vbuf[i % 3]
@@ -236,10 +241,10 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // key) and columns 16 (c / 16) + 4 (lane % 16 % 4) (+ 32 mb).
     const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VS + 16 * (c >> 4) + 4 * (lane & 3);
     u32x4_t kreg[G::KCH], vreg[G::KCH];
-    f32x16_t s_a[2], s_b[2];
-    v8 p_a[2][2], p_b[2][2];  // P^T operands [score block][K-step] of two consecutive tiles
+    f32x16_t s_a[NSB], s_b[NSB];
+    v8 p_a[NSB][2], p_b[NSB][2];  // P^T operands [score block][K-step] of two consecutive tiles
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) p_a[sb][t] = bitcast<v8>(u32x4_t{0u, 0u, 0u, 0u});
     auto tile = [&](int jj) { return min(jj, nkt - 1) * BC; };  // clamped first key of a tile
@@ -264,7 +269,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     }
 
     // O^T += V^T P^T for one tile whose V is in Vs (transpose reads).
-    auto pv = [&](const T *Vs, const v8 (&pp)[2][2]) {
+    auto pv = [&](const T *Vs, const v8 (&pp)[NSB][2]) {
         Vs += tr_off;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
@@ -294,8 +299,8 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // so the only waits on global loads are for data requested a full tile
     // earlier.  Tiles past a wave's causal limit are processed fully masked
     // (weight 0), which keeps the hot block free of branches.
-    auto step = [&](int j, int vb, f32x16_t (&sc)[2], f32x16_t (&sn)[2], const v8 (&pp)[2][2],
-                    v8 (&pc)[2][2]) {
+    auto step = [&](int j, int vb, f32x16_t (&sc)[NSB], f32x16_t (&sn)[NSB], const v8 (&pp)[NSB][2],
+                    v8 (&pc)[NSB][2]) {
         const int vprev = vb == 0 ? 2 : vb - 1, vnext = vb == 2 ? 0 : vb + 1;
         const int j0 = j * BC;
         // ---- mask: ragged last tile, the diagonal band and beyond (causal) ----
@@ -366,7 +371,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                 ts[qb] = 0.f;
             }
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
+            for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int qb = sb / NKB;
@@ -392,12 +397,12 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, sn);
         pv(Vbuf[vprev], pp);
         make_p();
-        constexpr int N_MFMA = 2 * (D / 16) + 2 * (D / 32) * 2;
+        constexpr int N_MFMA = NSB * D / 8;
         __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (D / 16) + 2 * (D / 32) * NKB * 2, 0);  // LDS reads
 #pragma unroll
         for (int i = 0; i < N_MFMA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);             // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x0002, 112 / N_MFMA, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x0002, 56 * NSB / N_MFMA, 0);  // VALU
         }
 
         // Range check: exponentials above 2^64 per tile (or inf/NaN) mean the
