@@ -119,6 +119,10 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     if (PAGED) nk_b = max(0, min(pc.seq_lens[b], pc.max_pages * pc.page_size));
     const int kbeg = split * chunk;
     const int kend = min(nk_b, kbeg + chunk);
+    // Paged, split: a split wholly past this sequence's length writes nothing
+    // (the merge reads only the splits that hold keys); split 0 always writes,
+    // so an empty sequence still gets O = 0, LSE = -inf.  Uniform per workgroup.
+    if (PAGED && splits > 1 && split > 0 && kbeg >= nk_b) return;
     const size_t kvoff = PAGED ? 0 : (size_t)bk * Nk * D;
     const T *Kb = K + kvoff;
     const T *Vb = V + kvoff;
@@ -326,18 +330,27 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
 // One wave per (b, h); lane d accumulates output column d (and d + 64).
 // The per-split LSEs are wave-uniform, so every lane reads all of them
 // (scalar loads) and no cross-lane reduction is needed; the partial rows are
-// loaded in batches of JB (addresses clamped to the last split, surplus rows
-// weighted 0), the first batch before the LSEs are even looked at.
+// loaded in batches of JB (addresses clamped to the last split read, surplus
+// rows weighted 0), the first batch before the LSEs are even looked at.  For
+// a paged cache only the splits that hold keys of the sequence are read (the
+// sweep skips the others without writing).
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_lse,
-                    T *__restrict__ O, float *__restrict__ LSE, int BH, int splits)
+                    T *__restrict__ O, float *__restrict__ LSE, int BH, int splits,
+                    const int *__restrict__ seq_lens, int H, int chunk, int cap)
 {
     constexpr int DPL = D / 64;  // output columns per lane
     constexpr int JB = 16;
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (bh >= BH) return;
+    // paged: only the splits that hold keys of this sequence were written
+    int nsp = splits;
+    if (seq_lens != nullptr) {
+        const int len = max(0, min(seq_lens[bh / H], cap));
+        nsp = max(1, min(splits, (len + chunk - 1) / chunk));
+    }
     const float *pl = part_lse + (size_t)bh * splits;
     const float *po = part_o + (size_t)bh * splits * D + lane;
 
@@ -345,27 +358,27 @@ decode_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ 
     auto load_batch = [&](int s1) {
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-            const int sj = min(s1 + j, splits - 1);
+            const int sj = min(s1 + j, nsp - 1);
 #pragma unroll
             for (int i = 0; i < DPL; ++i) vb[j][i] = po[(size_t)sj * D + 64 * i];
         }
     };
     load_batch(0);
     float M_ = -INFINITY;
-    for (int s = 0; s < splits; s += 8) {
+    for (int s = 0; s < nsp; s += 8) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) M_ = fmaxf(M_, pl[min(s + j, splits - 1)]);
+        for (int j = 0; j < 8; ++j) M_ = fmaxf(M_, pl[min(s + j, nsp - 1)]);
     }
     float acc[DPL], L = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
     if (M_ != -INFINITY) {
-        for (int s0 = 0; s0 < splits; s0 += JB) {
+        for (int s0 = 0; s0 < nsp; s0 += JB) {
             if (s0 > 0) load_batch(s0);
 #pragma unroll
             for (int j = 0; j < JB; ++j) {
                 const int sj = s0 + j;
-                const float wj = sj < splits ? fast_exp2((pl[min(sj, splits - 1)] - M_) * kLog2e) : 0.f;
+                const float wj = sj < nsp ? fast_exp2((pl[min(sj, nsp - 1)] - M_) * kLog2e) : 0.f;
                 L += wj;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) acc[i] += wj * vb[j][i];
@@ -401,7 +414,9 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
     if (e != hipSuccess || p.splits == 1) return e;
     const int BH = p.B * p.H;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0,
-                       st, p.part_o, p.part_lse, static_cast<T *>(p.o), p.lse, BH, p.splits);
+                       st, p.part_o, p.part_lse, static_cast<T *>(p.o), p.lse, BH, p.splits,
+                       p.block_table != nullptr ? p.seq_lens : nullptr, p.H, p.chunk,
+                       p.max_pages * p.page_size);
     return hipGetLastError();
 }
 

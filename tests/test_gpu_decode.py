@@ -199,3 +199,27 @@ def test_paged_full_length_equals_contiguous_and_clamps():
                              torch.from_numpy(table).cuda(), lens, scale=0.125, num_splits=splits)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_ragged_poisoned_workspace_many_splits():
+    """Splits past a sequence's end write nothing and the merge must not read
+    them: the whole workspace starts as NaN, lengths are ragged (one empty),
+    eight splits are forced."""
+    need_gpu()
+    B, H, Hkv, d, ps = 4, 8, 2, 64, 64
+    lens = [0, 1, 200, 1500]
+    announce(f"fa_decode_paged poisoned workspace, 8 splits, lens={lens}")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, lens, ps, d, "bf16", seed=8)
+    ws = fa.decode_workspace(B, H, Hkv, max_pages * ps, d, 8)
+    ws.fill_(255)
+    o, lse = fa.decode_paged(to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=0.125,
+                             num_splits=8, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    for b in range(1, B):
+        L = lens[b]
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], "bf16"), widen(k[b:b + 1, :, :L], "bf16"),
+                                        widen(v[b:b + 1, :, :L], "bf16"), False, 0.125)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, "bf16", f"paged poisoned b={b}")
