@@ -92,14 +92,18 @@ def _dist(fn, n, torch):
 def _sweep(torch, fa, fagen, to_dev, dev):
     """Sequence-length sweep of [MM] "La medicion" at the op level: the
     trading-model inputs (AR(1) + noise, 12 heads, causal, bf16) at
-    N = 512, 4,096 and 32,768, for head dims 64 and 128.  For each N: fa_fwd and fa_fwd + fa_bwd time and
+    N = 512, 4,096 and 32,768, for head dims 64, 128 and 256 (the head size
+    systems-analysis.info "FlashAttention (IT)" lists among FlashAttention-2's
+    additions, section "Evoluzione e sviluppi successivi").  For each N: fa_fwd
+    and fa_bwd time (fa_bwd at d = 64 and 128) and
     the extra device memory each call allocates, against the materialised
     definition (scores, softmax and P V as separate bf16 tensor ops, the
     standard path of [MM] "Por que la atencion esta ligada a la memoria"),
     forward only."""
     res = {"metric": "op cost vs sequence length (fa_fwd / fa_bwd vs materialised attention)",
            "data": "synthetic AR(1) phi=0.9 + N(0,0.1), seed 0", "dtype": "bf16", "rows": []}
-    for d, N in ((64, 512), (64, 4096), (64, 32768), (128, 512), (128, 4096), (128, 32768)):
+    for d, N in ((64, 512), (64, 4096), (64, 32768), (128, 512), (128, 4096), (128, 32768),
+                 (256, 512), (256, 4096), (256, 32768)):
         cfg = dict(B=1, H=12, Hkv=12, Nq=N, Nk=N, d=d, dtype="bf16", kind="ar1")
         qn, kn, vn = fagen.make_inputs(cfg, 0)
         q, k, v = (to_dev(x, "bf16") for x in (qn, kn, vn))
@@ -118,13 +122,17 @@ def _sweep(torch, fa, fagen, to_dev, dev):
         it = max(3, min(200, int(2e12 / flops)))
         (o, lse), mem_f = peak(lambda: fa.fwd(q, k, v, causal=True, scale=scale))
         ms_f = _timed(lambda i: fa.fwd(q, k, v, causal=True, scale=scale), it, 3, torch)
-        g = torch.empty_like(q).normal_(generator=torch.Generator(device=dev).manual_seed(1))
-        _, mem_b = peak(lambda: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale))
-        ms_b = _timed(lambda i: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale), it, 3, torch)
         row["fa_fwd"] = {"ms": round(ms_f, 4), "tflops": round(flops / (ms_f * 1e-3) / 1e12, 1),
                          "extra_bytes": int(mem_f)}
-        row["fa_bwd"] = {"ms": round(ms_b, 4), "tflops": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 1),
-                         "extra_bytes": int(mem_b)}
+        g = torch.empty_like(q).normal_(generator=torch.Generator(device=dev).manual_seed(1))
+        if d <= 128:
+            _, mem_b = peak(lambda: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale))
+            ms_b = _timed(lambda i: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale), it, 3, torch)
+            row["fa_bwd"] = {"ms": round(ms_b, 4),
+                             "tflops": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 1),
+                             "extra_bytes": int(mem_b)}
+        else:
+            row["fa_bwd"] = None  # the backward kernels take d = 64 and 128
         kt = k.transpose(-1, -2).contiguous()
         mask = torch.ones(N, N, dtype=torch.bool, device=dev).triu(1)
 

@@ -50,10 +50,13 @@ fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 constexpr long long kMaxSlice = (1LL << 31) - 1;
 
 // Shape checks common to the forward entry points (pointers checked apart).
-fa_status check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale)
+// Every entry point takes d = 64 and 128; `allow256` admits d = 256 (the
+// bf16/fp16 forward only).
+fa_status check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                          bool allow256 = false)
 {
     if (B < 0 || H < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (d != 64 && d != 128 && !(allow256 && d == 256)) return FA_ERR_HEADDIM;
     if (H % Hkv != 0) return FA_ERR_GQA;
     if ((long long)Nq * d > kMaxSlice || (long long)Nk * d > kMaxSlice) return FA_ERR_SHAPE;
     const long long qtiles = ((long long)Nq + fa::kFwdQTile - 1) / fa::kFwdQTile;
@@ -125,7 +128,7 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
                  int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
                  void *stream)
 {
-    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale);
+    fa_status s = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype == FA_F16 || dtype == FA_BF16);
     if (s != FA_OK) return s;
     if ((s = check_fwd_ptrs(q, k, v, o, lse, B, Nq, Nk)) != FA_OK) return s;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
@@ -166,6 +169,8 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
 
 int fa_kv_tile(fa_dtype dtype, int d, int pcast)
 {
+    if (d == 256 && !pcast && (dtype == FA_F16 || dtype == FA_BF16))
+        return fa::fwd_mfma_kv_tile(d, 1, 1, 1LL << 30);
     if (d != 64 && d != 128) return -1;
     if (dtype == FA_F32 || (pcast && dtype == FA_BF16)) return fa::fwd_f32_kv_tile(d);
     if (pcast) return -1;
@@ -362,7 +367,7 @@ const char *fa_status_str(fa_status s)
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size, H/Hkv < 1, or a tensor slice too large";
-    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128 (256: bf16/fp16 forward only)";
     case FA_ERR_GQA: return "FA_ERR_GQA: H must be a multiple of Hkv";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype not supported by this entry point";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";

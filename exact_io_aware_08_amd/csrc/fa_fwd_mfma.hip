@@ -79,7 +79,7 @@ template <> struct Pack2<_Float16> {
 
 // Geometry for head dim D and QB query blocks per wave.
 template <int D, int QB> struct Geo {
-    static constexpr int NKB = (QB >= 2 || D == 128) ? 1 : 2;  // 32-key blocks per KV tile
+    static constexpr int NKB = (QB >= 2 || D >= 128) ? 1 : 2;  // 32-key blocks per KV tile
     // (d = 128 with 64-key tiles needed 96 KB of LDS: one workgroup, one wave
     //  per SIMD, 1.5x slower than two waves with 32-key tiles)
     static constexpr int NSB = QB * NKB;         // 32x32 score blocks per wave
@@ -87,10 +87,10 @@ template <int D, int QB> struct Geo {
     static constexpr int BR = NW * 32 * QB;      // queries per workgroup
     static constexpr int KSTR = D + 8;           // K tile row stride in LDS (elements)
     // V tile row stride in LDS (elements): 48 dwords at d = 64, 80 at d =
-    // 128, i.e. 16 (mod 64) banks apart per row pair, so the four rows times
-    // four 8-byte column chunks that a half-wave's transpose read touches
-    // fall in distinct banks.
-    static constexpr int VS = D == 64 ? 96 : 160;
+    // 128, 144 at d = 256, i.e. 16 (mod 32) banks apart per row, so the four
+    // rows times four 8-byte column chunks that a half-wave's transpose read
+    // touches fall in distinct banks.
+    static constexpr int VS = D == 64 ? 96 : D == 128 ? 160 : 288;
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     static constexpr int KCH = BC * CPR / 256;   // K (and V) chunks per thread per tile
     static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "staging split");
@@ -170,7 +170,7 @@ __device__ __forceinline__ float sum_pair(float x)
 }
 
 template <typename T, int D, int QB, bool CAUSAL>
-__global__ void __launch_bounds__(256, QB >= 3 ? 1 : 2)
+__global__ void __launch_bounds__(256, (QB >= 3 || D >= 256) ? 1 : 2)
 fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                 T *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk,
                 int n_bh, int n_qtiles, float scale, float scale_log2)
@@ -500,6 +500,7 @@ hipError_t launch_t(const FwdProblem &p, hipStream_t st)
 template <typename T, bool CAUSAL>
 hipError_t launch_c(const FwdProblem &p, hipStream_t st)
 {
+    if (p.d == 256) return launch_t<T, 256, 1, CAUSAL>(p, st);
     if (p.d == 128) return launch_t<T, 128, 1, CAUSAL>(p, st);
     return qb_for(64, p.B, p.H, p.Nq) == 2 ? launch_t<T, 64, 2, CAUSAL>(p, st)
                                             : launch_t<T, 64, 1, CAUSAL>(p, st);
@@ -515,6 +516,7 @@ hipError_t launch_dt(const FwdProblem &p, hipStream_t st)
 
 int fwd_mfma_kv_tile(int d, long long B, long long H, long long Nq)
 {
+    if (d == 256) return Geo<256, 1>::BC;
     if (d == 128) return Geo<128, 1>::BC;
     return qb_for(64, B, H, Nq) == 2 ? Geo<64, 2>::BC : Geo<64, 1>::BC;
 }

@@ -60,7 +60,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
     FA_ERR_SHAPE = 2,     /* negative size, H or Hkv < 1, or a slice too large   */
-    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                  */
+    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 (fa_fwd bf16/fp16: or 256)       */
     FA_ERR_GQA = 4,       /* H is not a multiple of Hkv                          */
     FA_ERR_DTYPE = 5,     /* dtype not supported by this entry point            */
     FA_ERR_ALIGN = 6,     /* a tensor pointer is not 16-byte aligned             */
@@ -76,6 +76,10 @@ typedef enum {
  *   q, k, v : device inputs, layout above, element type `dtype`
  *             (FA_BF16 and FA_F16 run on bf16/fp16 MFMA with fp32
  *             accumulation; FA_F32 runs on fp32 MFMA).
+ *   d       : 64 or 128 for every dtype; also 256 for FA_BF16 and FA_F16
+ *             (the head size FlashAttention-2 added, systems-analysis.info
+ *             "FlashAttention (IT)", section "Evoluzione e sviluppi
+ *             successivi").  Other values return FA_ERR_HEADDIM.
  *   o       : device output [B, H, Nq, d], same dtype as the inputs.
  *   lse     : device output [B, H, Nq] fp32, or NULL to skip it.
  *   causal  : 0 = full attention, 1 = bottom-right causal mask.
@@ -126,7 +130,7 @@ fa_status fa_fwd_pcast(const void *q, const void *k, const void *v, void *o, flo
  * d = 64 the width also depends on the grid -- 32 keys when at least 1024
  * workgroups of 256 query rows exist (ceil(Nq/256)*B*H >= 1024), else 64 --
  * and this returns the large-grid value; their results depend on it only
- * through rounding order. */
+ * through rounding order.  At d = 128 and 256 (16-bit only) it is 32. */
 int fa_kv_tile(fa_dtype dtype, int d, int pcast);
 
 /*

@@ -65,7 +65,9 @@ def _fwd(**kw):
     (dict(B=-1), "FA_ERR_SHAPE"), (dict(H=0), "FA_ERR_SHAPE"), (dict(Hkv=0), "FA_ERR_SHAPE"),
     (dict(Nq=-3), "FA_ERR_SHAPE"), (dict(Nk=-1), "FA_ERR_SHAPE"),
     (dict(Nq=(1 << 31) // 64), "FA_ERR_SHAPE"),
-    (dict(d=96), "FA_ERR_HEADDIM"), (dict(d=256), "FA_ERR_HEADDIM"),
+    (dict(d=96), "FA_ERR_HEADDIM"), (dict(d=512), "FA_ERR_HEADDIM"),
+    (dict(d=256, dtype=F32), "FA_ERR_HEADDIM"), (dict(d=256, B=0), "FA_OK"),
+    (dict(d=256, dtype=F16, Nq=0), "FA_OK"),
     (dict(H=3, Hkv=2), "FA_ERR_GQA"),
     (dict(dtype=7), "FA_ERR_DTYPE"),
     (dict(scale=0.0), "FA_ERR_SCALE"), (dict(scale=-1.0), "FA_ERR_SCALE"),
@@ -92,7 +94,8 @@ def _pcast(**kw):
     (dict(dtype=F16), "FA_ERR_DTYPE"),
     (dict(p_scale=0.0), "FA_ERR_SCALE"), (dict(p_scale=512.0), "FA_ERR_SCALE"),
     (dict(rev=4), "FA_ERR_ARG"), (dict(rev=-1), "FA_ERR_ARG"), (dict(n_sink=-1), "FA_ERR_ARG"),
-    (dict(d=32), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
+    (dict(d=32), "FA_ERR_HEADDIM"), (dict(d=256), "FA_ERR_HEADDIM"),
+    (dict(d=256, dtype=BF16), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
 ])
 def test_pcast_validation(kw, expect):
     assert _pcast(**kw) == S[expect]
@@ -113,7 +116,7 @@ def _decode(ws_bytes=None, **kw):
     (dict(ws_bytes=16), "FA_ERR_WORKSPACE"), (dict(ws=PM), "FA_ERR_ALIGN"),
     (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(splits=-1), "FA_ERR_ARG"),
     (dict(splits=5000), "FA_ERR_ARG"), (dict(H=6, Hkv=4), "FA_ERR_GQA"),
-    (dict(d=80), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
+    (dict(d=80), "FA_ERR_HEADDIM"), (dict(d=256), "FA_ERR_HEADDIM"), (dict(B=0), "FA_OK"),
 ])
 def test_decode_validation(kw, expect):
     assert _decode(**kw) == S[expect]
@@ -143,6 +146,9 @@ def test_kv_tile_and_cast_validation():
     assert lib.fa_kv_tile(BF16, 64, 1) == lib.fa_kv_tile(F32, 64, 1)
     assert lib.fa_kv_tile(F16, 64, 1) == -1
     assert lib.fa_kv_tile(F32, 48, 0) == -1
+    # d = 256: the 16-bit forward only (32-key tiles)
+    assert lib.fa_kv_tile(BF16, 256, 0) == 32 and lib.fa_kv_tile(F16, 256, 0) == 32
+    assert lib.fa_kv_tile(F32, 256, 0) == -1 and lib.fa_kv_tile(BF16, 256, 1) == -1
     assert lib.fa_cast_e4m3(None, None, None, 4, None) == S["FA_ERR_NULL"]
     assert lib.fa_cast_e4m3(None, None, None, 0, None) == S["FA_OK"]
 
@@ -170,7 +176,7 @@ def _bwd(ws_bytes=None, **kw):
     (dict(o=None), "FA_ERR_NULL"), (dict(dk=None), "FA_ERR_NULL"), (dict(dv=None), "FA_ERR_NULL"),
     (dict(dq=None), "FA_ERR_NULL"), (dict(do=PM), "FA_ERR_ALIGN"), (dict(dv=PM), "FA_ERR_ALIGN"),
     (dict(ws=None), "FA_ERR_WORKSPACE"), (dict(ws_bytes=8), "FA_ERR_WORKSPACE"),
-    (dict(ws=PM), "FA_ERR_ALIGN"), (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(d=32), "FA_ERR_HEADDIM"),
+    (dict(ws=PM), "FA_ERR_ALIGN"), (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(d=32), "FA_ERR_HEADDIM"), (dict(d=256), "FA_ERR_HEADDIM"),
     (dict(H=6, Hkv=4), "FA_ERR_GQA"), (dict(scale=0.0), "FA_ERR_SCALE"), (dict(causal=3), "FA_ERR_ARG"),
     (dict(B=-1), "FA_ERR_SHAPE"), (dict(B=0), "FA_OK"), (dict(Nq=0, Nk=0), "FA_OK"),
 ])

@@ -85,6 +85,23 @@ def test_dtypes_and_head_dims(dt, d):
     run_case(1, 2, 2, 257, 257, d, dt, False, seed=8)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_head_dim_256(dt):
+    """d = 256 (16-bit types only): causal and full, ragged query and key
+    tails, GQA, Nq != Nk."""
+    run_case(2, 4, 2, 300, 300, 256, dt, True, seed=11)
+    run_case(1, 2, 1, 257, 257, 256, dt, False, seed=12)
+    run_case(1, 2, 2, 100, 333, 256, dt, True, seed=13)
+    run_case(1, 2, 2, 1, 65, 256, dt, False, seed=14)
+
+
+def test_head_dim_256_long_sampled():
+    """B=1, H=8, Hkv=2, N=4,096, d=256, bf16, causal, AR(1) inputs: 96 sampled
+    rows per head plus the first and last row."""
+    rows = _sampled_rows(1, 8, 4096, 96, seed=3)
+    run_case(1, 8, 2, 4096, 4096, 256, "bf16", True, kind="ar1", rows=rows)
+
+
 @pytest.mark.parametrize("Nq,Nk", [(100, 333), (333, 100), (300, 130), (1, 700), (129, 1)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_nq_ne_nk(Nq, Nk, causal):
