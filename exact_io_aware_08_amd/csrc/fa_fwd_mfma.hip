@@ -18,7 +18,9 @@
 // query rows of one (b, h); a KV tile has NKB blocks of 32 keys; QB*NKB = 2
 // score blocks per wave at d = 64, one at d = 128, where a 32-key tile keeps
 // the LDS of a workgroup at 48 KB and the registers under 256, so two waves
-// share each SIMD):
+// share each SIMD; at d = 256 a workgroup has 8 waves and two waves share
+// each query block, each holding the Q operand and O accumulator of one
+// half of d and exchanging partial scores through LDS once per tile):
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16:
 //    the fp32 result gives lane l the 16 keys {8i + 4(l/32) + r} of query
 //    l%32 per 32x32 block, so a row's max needs one v_permlane32_swap and
@@ -55,8 +57,6 @@
 namespace fa {
 namespace {
 
-constexpr int NW = 4;         // waves per workgroup
-
 // Row-sum accumulation of one converted pair of probabilities.  For fp16
 // the sum is taken over the converted values with v_dot2 (an 11-bit
 // mantissa keeps the normaliser within 2^-12 relative); bf16 keeps only 8
@@ -79,12 +79,19 @@ template <> struct Pack2<_Float16> {
 
 // Geometry for head dim D and QB query blocks per wave.
 template <int D, int QB> struct Geo {
+    // d = 256: two waves share each query block, each holding the Q operand
+    // and the O accumulator of one half of d (DS = 2), so a wave fits in 256
+    // registers and two waves share each SIMD.
+    static constexpr int DS = D >= 256 ? 2 : 1;  // waves per query block
+    static constexpr int DW = D / DS;            // head-dim columns per wave
+    static constexpr int NW = 4 * DS;            // waves per workgroup
+    static constexpr int NT = 64 * NW;           // threads per workgroup
     static constexpr int NKB = (QB >= 2 || D >= 128) ? 1 : 2;  // 32-key blocks per KV tile
     // (d = 128 with 64-key tiles needed 96 KB of LDS: one workgroup, one wave
     //  per SIMD, 1.5x slower than two waves with 32-key tiles)
     static constexpr int NSB = QB * NKB;         // 32x32 score blocks per wave
     static constexpr int BC = 32 * NKB;          // keys per KV tile
-    static constexpr int BR = NW * 32 * QB;      // queries per workgroup
+    static constexpr int BR = 4 * 32 * QB;       // queries per workgroup
     static constexpr int KSTR = D + 8;           // K tile row stride in LDS (elements)
     // V tile row stride in LDS (elements): 48 dwords at d = 64, 80 at d =
     // 128, 144 at d = 256, i.e. 16 (mod 32) banks apart per row, so the four
@@ -92,13 +99,14 @@ template <int D, int QB> struct Geo {
     // touches fall in distinct banks.
     static constexpr int VS = D == 64 ? 96 : D == 128 ? 160 : 288;
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-    static constexpr int KCH = BC * CPR / 256;   // K (and V) chunks per thread per tile
-    static_assert(KCH >= 1 && KCH * 256 == BC * CPR, "staging split");
+    static constexpr int KCH = BC * CPR / NT;    // K (and V) chunks per thread per tile
+    static_assert(KCH >= 1 && KCH * NT == BC * CPR, "staging split");
+    static_assert(DS == 1 || NSB == 1, "d split with one score block per wave");
     static_assert(VS >= D && (VS * 2) % 16 == 0, "V row stride");
 };
 
 // Per-thread offsets of the staging loads and LDS stores within a tile:
-// chunk ci = tid + 256 r -> row ci / CPR, chunk ci % CPR (row-major,
+// chunk ci = tid + NT r -> row ci / CPR, chunk ci % CPR (row-major,
 // coalesced).  K and V use the same map, with their own LDS row strides.
 template <int D, int QB> struct KvMap {
     using G = Geo<D, QB>;
@@ -108,7 +116,7 @@ template <int D, int QB> struct KvMap {
     __device__ __forceinline__ KvMap(int tid, int elem_bytes) {
 #pragma unroll
         for (int r = 0; r < G::KCH; ++r) {
-            const int ci = tid + r * 256;
+            const int ci = tid + r * G::NT;
             off[r] = ((ci / G::CPR) * D + (ci % G::CPR) * 8) * elem_bytes;
             kst[r] = (ci / G::CPR) * G::KSTR + (ci % G::CPR) * 8;
             vst[r] = (ci / G::CPR) * G::VS + (ci % G::CPR) * 8;
@@ -135,11 +143,13 @@ __device__ __forceinline__ void store_rows(T *buf, const int (&st)[Geo<D, QB>::K
     for (int r = 0; r < Geo<D, QB>::KCH; ++r) *reinterpret_cast<u32x4_t *>(&buf[st[r]]) = reg[r];
 }
 
-// S^T blocks (32 keys x 32 queries each) = K_tile Q_wave^T; block index
-// qb * NKB + kb.  Each K operand read serves all QB query blocks.
+// S^T blocks (32 keys x 32 queries each) = K_tile Q_wave^T over the wave's
+// head-dim columns [dbase, dbase + DW); block index qb * NKB + kb.  Each K
+// operand read serves all QB query blocks.
 template <typename T, int D, int QB>
-__device__ __forceinline__ void scores(const T *Ks, const typename Mma16<T>::v8 (&qop)[QB][D / 16],
-                                       int c, int hh, f32x16_t (&s)[Geo<D, QB>::NSB])
+__device__ __forceinline__ void scores(const T *Ks,
+                                       const typename Mma16<T>::v8 (&qop)[QB][Geo<D, QB>::DW / 16],
+                                       int c, int hh, int dbase, f32x16_t (&s)[Geo<D, QB>::NSB])
 {
     using M = Mma16<T>;
     using v8 = typename M::v8;
@@ -149,8 +159,8 @@ __device__ __forceinline__ void scores(const T *Ks, const typename Mma16<T>::v8 
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            const v8 kop = *reinterpret_cast<const v8 *>(&Ks[(kb * 32 + c) * G::KSTR + 16 * t + 8 * hh]);
+        for (int t = 0; t < G::DW / 16; ++t) {
+            const v8 kop = *reinterpret_cast<const v8 *>(&Ks[(kb * 32 + c) * G::KSTR + dbase + 16 * t + 8 * hh]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb * G::NKB + kb] = M::mma32(kop, qop[qb][t], s[qb * G::NKB + kb]);
         }
@@ -170,7 +180,7 @@ __device__ __forceinline__ float sum_pair(float x)
 }
 
 template <typename T, int D, int QB, bool CAUSAL>
-__global__ void __launch_bounds__(256, (QB >= 3 || D >= 256) ? 1 : 2)
+__global__ void __launch_bounds__((Geo<D, QB>::NT), (QB >= 3 ? 1 : 2))
 fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                 T *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk,
                 int n_bh, int n_qtiles, float scale, float scale_log2)
@@ -179,14 +189,19 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     using v8 = typename M::v8;
     using P2 = Pack2<T>;
     using G = Geo<D, QB>;
-    constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS, NSB = G::NSB;
+    constexpr int BC = G::BC, NKB = G::NKB, VS = G::VS, NSB = G::NSB, DS = G::DS, DW = G::DW;
 
     __shared__ __attribute__((aligned(16))) T Kbuf[2][BC * G::KSTR];
     __shared__ __attribute__((aligned(16))) T Vbuf[3][BC * VS];  // tile i in Vbuf[i % 3]
+    // d split: partial S^T exchange between the two waves of a query block,
+    // [tile parity][wave][register quad][lane] (one float4 per lane each)
+    __shared__ f32x4_t xbuf[DS > 1 ? 2 * G::NW * 4 * 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int wq = w / DS;                                   // query block of this wave
+    const int dbase = (w % DS) * DW;                         // its first head-dim column
 
     const int qt = n_qtiles - 1 - (int)(blockIdx.x / (unsigned)n_bh);
     const int bh = (int)(blockIdx.x % (unsigned)n_bh);
@@ -200,7 +215,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     T *Ob = O + qoff;
 
     const int q0 = qt * G::BR;
-    const int q0w = q0 + w * 32 * QB;  // first row of this wave
+    const int q0w = q0 + wq * 32 * QB;  // first row of this wave
     const int off = Nk - Nq;
     int nkt = (Nk + BC - 1) / BC;
     if (CAUSAL) {
@@ -208,26 +223,27 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         nkt = lim < 0 ? 0 : min(nkt, lim / BC + 1);
     }
 
-    // Q operand (B of S^T = K Q^T): lane (c, hh) holds Q[q0w + 32qb + c][16t + 8hh + e].
-    // Rows past Nq read as zeros (buffer range check); they are never stored.
-    v8 qop[QB][D / 16];
+    // Q operand (B of S^T = K Q^T): lane (c, hh) holds
+    // Q[q0w + 32qb + c][dbase + 16t + 8hh + e].  Rows past Nq read as zeros
+    // (buffer range check); they are never stored.
+    v8 qop[QB][DW / 16];
     {
         const __amdgpu_buffer_rsrc_t rq = rows_rsrc<T, D>(Qb, Nq, q0w);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int t = 0; t < D / 16; ++t)
+            for (int t = 0; t < DW / 16; ++t)
                 qop[qb][t] = bitcast<v8>(__builtin_amdgcn_raw_buffer_load_b128(
-                    rq, ((32 * qb + c) * D + 16 * t + 8 * hh) * (int)sizeof(T), 0, 0));
+                    rq, ((32 * qb + c) * D + dbase + 16 * t + 8 * hh) * (int)sizeof(T), 0, 0));
             settle(qop[qb]);
         }
     }
 
-    f32x16_t acc[QB][D / 32];
+    f32x16_t acc[QB][DW / 32];  // O^T rows dbase + 32 i + (register layout)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[qb][i] = f32x16_t{};
+        for (int i = 0; i < DW / 32; ++i) acc[qb][i] = f32x16_t{};
     float m_ref[QB], l_run[QB];  // reference max (raw units; same in lanes l, l^32), row-sum share
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -249,13 +265,33 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         for (int t = 0; t < 2; ++t) p_a[sb][t] = bitcast<v8>(u32x4_t{0u, 0u, 0u, 0u});
     auto tile = [&](int jj) { return min(jj, nkt - 1) * BC; };  // clamped first key of a tile
 
+    // d split: publish this wave's partial S^T of a tile, and add the other
+    // wave's (same lane layout; x + y == y + x, so both waves then hold the
+    // same scores bit for bit and take the same softmax decisions).  Buffer
+    // tile & 1 is written before the barrier that ends the previous step and
+    // read after it; its next write comes after the following barrier.
+    auto x_put = [&](int par, const f32x16_t (&sp)[NSB]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xbuf[((par * G::NW + w) * 4 + i) * 64 + lane] =
+                f32x4_t{sp[0][4 * i], sp[0][4 * i + 1], sp[0][4 * i + 2], sp[0][4 * i + 3]};
+    };
+    auto x_add = [&](int par, f32x16_t (&sp)[NSB]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4_t o = xbuf[((par * G::NW + (w ^ 1)) * 4 + i) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sp[0][4 * i + e] += o[e];
+        }
+    };
+
     if (nkt > 0) {
         // prologue: K0 -> Kbuf[0], V0 -> Vbuf[0], K1 -> Kbuf[1]; registers
         // then hold K2 and V1.  Vbuf[2] stands for tile -1, whose (zero) P
         // is multiplied in the first step: it must hold finite values.
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, 0), mp, kreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, 0), mp, vreg);
-        for (int i = tid; i < BC * VS / 8; i += 256)
+        for (int i = tid; i < BC * VS / 8; i += G::NT)
             reinterpret_cast<u32x4_t *>(Vbuf[2])[i] = u32x4_t{0u, 0u, 0u, 0u};
         store_rows<T, D, QB>(Kbuf[0], mp.kst, kreg);
         store_rows<T, D, QB>(Vbuf[0], mp.vst, vreg);
@@ -264,7 +300,8 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         store_rows<T, D, QB>(Kbuf[1], mp.kst, kreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(2)), mp, kreg);
         lds_barrier();
-        scores<T, D, QB>(Kbuf[0], qop, c, hh, s_a);
+        scores<T, D, QB>(Kbuf[0], qop, c, hh, dbase, s_a);
+        if (DS > 1) x_put(0, s_a);
         lds_barrier();  // Kbuf[0] is overwritten in iteration 0
     }
 
@@ -272,14 +309,14 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     auto pv = [&](const T *Vs, const v8 (&pp)[NSB][2]) {
         Vs += tr_off;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
+        for (int mb = 0; mb < DW / 32; ++mb)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     // K-slots 0-3: keys 16t + 4hh + 0..3, slots 4-7: 16t + 8 + 4hh + 0..3
-                    // (of block kb), column d = 32 mb + c: the S^T register order.
-                    const T *vp = Vs + (kb * 32 + 16 * t) * VS + 32 * mb;
+                    // (of block kb), column d = dbase + 32 mb + c: the S^T register order.
+                    const T *vp = Vs + (kb * 32 + 16 * t) * VS + dbase + 32 * mb;
                     const u32x2_t lo = read_tr(vp);
                     const u32x2_t hi = read_tr(vp + 8 * VS);
                     const v8 vop = bitcast<v8>(u32x4_t{lo.x, lo.y, hi.x, hi.y});
@@ -303,6 +340,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                     v8 (&pc)[NSB][2]) {
         const int vprev = vb == 0 ? 2 : vb - 1, vnext = vb == 2 ? 0 : vb + 1;
         const int j0 = j * BC;
+        if (DS > 1) x_add(j & 1, sc);  // full S^T of tile j
         // ---- mask: ragged last tile, the diagonal band and beyond (causal) ----
         const bool need_mask = (j0 + BC > Nk) || (CAUSAL && j0 + BC - 1 > q0w + off);
         if (need_mask) {
@@ -357,7 +395,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                 m_ref[qb] = raise ? m : m_ref[qb];
                 l_run[qb] *= alpha;
 #pragma unroll
-                for (int i = 0; i < D / 32; ++i) acc[qb][i] *= alpha;
+                for (int i = 0; i < DW / 32; ++i) acc[qb][i] *= alpha;
             }
         };
 
@@ -394,11 +432,11 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 
         // ---- hot block: S^T of tile j+1 and P V of tile j-1 on the MFMA
         //      pipe while the VALU turns tile j into P ----
-        scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, sn);
+        scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, dbase, sn);
         pv(Vbuf[vprev], pp);
         make_p();
-        constexpr int N_MFMA = NSB * D / 8;
-        __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (D / 16) + 2 * (D / 32) * NKB * 2, 0);  // LDS reads
+        constexpr int N_MFMA = NSB * DW / 8;
+        __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (DW / 16) + 2 * (DW / 32) * NKB * 2, 0);  // LDS reads
 #pragma unroll
         for (int i = 0; i < N_MFMA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);             // 1 MFMA
@@ -416,6 +454,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] += ts[qb];
+        if (DS > 1) x_put((j + 1) & 1, sn);  // partial S^T of tile j+1
 
         // ---- staging of the next tiles into buffers not read in this step ----
         store_rows<T, D, QB>(Kbuf[j & 1], mp.kst, kreg);
@@ -452,10 +491,10 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             const float inv = l > 0.f ? 1.f / l : 0.f;
             typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
+            for (int mb = 0; mb < DW / 32; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int d0 = 32 * mb + 8 * i + 4 * hh;
+                    const int d0 = dbase + 32 * mb + 8 * i + 4 * hh;
                     t4 vals;
                     vals[0] = static_cast<T>(acc[qb][mb][4 * i + 0] * inv);
                     vals[1] = static_cast<T>(acc[qb][mb][4 * i + 1] * inv);
@@ -463,7 +502,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                     vals[3] = static_cast<T>(acc[qb][mb][4 * i + 3] * inv);
                     *reinterpret_cast<t4 *>(Ob + (size_t)row * D + d0) = vals;
                 }
-            if (LSE != nullptr && hh == 0)
+            if (LSE != nullptr && hh == 0 && dbase == 0)
                 LSE[(size_t)bh * Nq + row] = l > 0.f ? m_ref[qb] * scale + logf(l) : -INFINITY;
         }
     }
@@ -489,7 +528,7 @@ hipError_t launch_t(const FwdProblem &p, hipStream_t st)
     using G = Geo<D, QB>;
     const int n_qtiles = (p.Nq + G::BR - 1) / G::BR;
     const int n_bh = p.B * p.H;
-    const dim3 grid((unsigned)n_qtiles * (unsigned)n_bh), block(256);
+    const dim3 grid((unsigned)n_qtiles * (unsigned)n_bh), block(G::NT);
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, QB, CAUSAL>), grid, block, 0, st,
                        static_cast<const T *>(p.q), static_cast<const T *>(p.k),
                        static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.H, p.Hkv,
