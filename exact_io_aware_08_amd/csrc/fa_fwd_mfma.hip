@@ -431,7 +431,12 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         };
 
         // ---- hot block: S^T of tile j+1 and P V of tile j-1 on the MFMA
-        //      pipe while the VALU turns tile j into P ----
+        //      pipe while the VALU turns tile j into P.  It runs at raised
+        //      wave priority, so the other wave on the SIMD (another
+        //      workgroup) issues its staging, masking and barrier work in the
+        //      hot block's gaps rather than ahead of it (about 1.5% faster on
+        //      the trading-day prefill) ----
+        __builtin_amdgcn_s_setprio(1);
         scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, dbase, sn);
         pv(Vbuf[vprev], pp);
         make_p();
@@ -442,6 +447,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);             // 1 MFMA
             __builtin_amdgcn_sched_group_barrier(0x0002, 56 * NSB / N_MFMA, 0);  // VALU
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // Range check: exponentials above 2^64 per tile (or inf/NaN) mean the
         // reference is far below this tile's scores; rebase and redo the tile.
