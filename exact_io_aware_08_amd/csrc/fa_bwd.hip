@@ -220,14 +220,24 @@ bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restr
             s = M::mma32(kop, qop[t], s);
             dp = M::mma32(vop, gop[t], dp);
         }
-        // P and dS for this tile (register r: key j*32 + 8(r/4) + 4hh + r%4)
+        // P and dS for this tile (register r: key j*32 + 8(r/4) + 4hh + r%4).
+        // Tiles whose every key every row of the wave sees (uniform test)
+        // skip the per-element mask; rows past Nq are never stored.
         const int j0 = j * TK;
         f32x16_t ds;
+        if (j0 + TK <= Nk && (!CAUSAL || j0 + TK - 1 <= q0w + off)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float p = (key < lim) ? fast_exp2(fmaf(s[r], scale_log2, -lse2)) : 0.f;
-            ds[r] = p * (dp[r] - drow);
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+                ds[r] = p * (dp[r] - drow);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float p = (key < lim) ? fast_exp2(fmaf(s[r], scale_log2, -lse2)) : 0.f;
+                ds[r] = p * (dp[r] - drow);
+            }
         }
         // dQ^T += K^T dS^T
 #pragma unroll
@@ -384,18 +394,36 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             dp = M::mma32(ga, vop[t], dp);
         }
         f32x16_t p, ds;
+        // Tiles where every query sees every key of the wave (uniform test)
+        // skip the per-element mask.
+        const bool full = q0 + TK <= Nq && k0w + TK <= Nk && (!CAUSAL || k0w + TK - 1 <= q0 + off);
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[buf][8 * i + 4 * hh]);
-            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[buf][8 * i + 4 * hh]);
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[buf][8 * i + 4 * hh]);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[buf][8 * i + 4 * hh]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * i + e;
-                const int q = q0 + 8 * i + 4 * hh + e;
-                const bool vis = q < Nq && key < Nk && (!CAUSAL || key <= q + off);
-                const float pv = vis ? fast_exp2(fmaf(s[r], scale_log2, -l4[e])) : 0.f;
-                p[r] = pv;
-                ds[r] = pv * (dp[r] - d4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * i + e;
+                    const float pv = fast_exp2(fmaf(s[r], scale_log2, -l4[e]));
+                    p[r] = pv;
+                    ds[r] = pv * (dp[r] - d4[e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[buf][8 * i + 4 * hh]);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[buf][8 * i + 4 * hh]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * i + e;
+                    const int q = q0 + 8 * i + 4 * hh + e;
+                    const bool vis = q < Nq && key < Nk && (!CAUSAL || key <= q + off);
+                    const float pv = vis ? fast_exp2(fmaf(s[r], scale_log2, -l4[e])) : 0.f;
+                    p[r] = pv;
+                    ds[r] = pv * (dp[r] - d4[e]);
+                }
             }
         }
         // dV^T += dO^T P,  dK^T += Q^T dS
