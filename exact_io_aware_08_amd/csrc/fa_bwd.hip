@@ -22,7 +22,9 @@
 //    per lane; P and dS, packed, are the B operands of dV^T += dO^T P and
 //    dK^T += Q^T dS, with dO^T and Q^T from transpose reads of the staged
 //    query tile.  A workgroup owns 128 keys of one KV head and sweeps every
-//    query tile of every query head of its group that sees those keys.
+//    query tile of every query head of its group that sees those keys; the
+//    sweep is software-pipelined (the S/dP products of the next query tile
+//    and the dV/dK products of the previous one overlap the P/dS work).
 // Scores, dP and all accumulators are fp32; P and dS are rounded to the
 // input type only as MFMA operands.
 #include "fa_device.hpp"
@@ -270,7 +272,7 @@ bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restr
 // it sweeps the query tiles of all G query heads of the group.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, D >= 128 ? 1 : 2)
 bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
                 const T *__restrict__ dO, const float *__restrict__ LSE,
                 const float *__restrict__ Dv, T *__restrict__ dK, T *__restrict__ dV, int H,
@@ -281,10 +283,10 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     using TM = TileMap<D>;
     constexpr int ST = TM::ST, BKEYS = NW * TK;
 
-    __shared__ __attribute__((aligned(16))) T Qbuf[2][TK * ST];
-    __shared__ __attribute__((aligned(16))) T Gbuf[2][TK * ST];      // dO
-    __shared__ __attribute__((aligned(16))) float Lbuf[2][TK];       // LSE * log2(e), 0 for rows without keys
-    __shared__ __attribute__((aligned(16))) float Dbuf[2][TK];
+    __shared__ __attribute__((aligned(16))) T Qbuf[4][TK * ST];      // iteration i in buffer i % 4
+    __shared__ __attribute__((aligned(16))) T Gbuf[4][TK * ST];      // dO
+    __shared__ __attribute__((aligned(16))) float Lbuf[4][TK];       // LSE * log2(e), 0 for rows without keys
+    __shared__ __attribute__((aligned(16))) float Dbuf[4][TK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
@@ -369,23 +371,33 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         else if (tid < 2 * TK) Dbuf[buf][tid - TK] = lreg;
     };
 
+    // Software pipeline over the iterations, as in the forward: step `it`
+    // issues the S/dP products of iteration it+1 and the dV/dK products of
+    // iteration it-1 on the MFMA pipe while the VALU turns S/dP of iteration
+    // it into P and dS.  Iteration i's query and dO tile, LSE and D live in
+    // buffer i % 4 from step i-2 (staging) to step i+1 (its dV/dK products);
+    // buffer 3 stands for iteration -1, whose operands are zero, and holds
+    // zeros so that its products stay finite.
     if (n_it > 0) {
         fetch(0);
         stage(0);
         fetch(1);
+        stage(1);
+        fetch(2);
+        for (int i = tid; i < TK * ST / 8; i += 256) {
+            reinterpret_cast<u32x4_t *>(Qbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4_t *>(Gbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
+        }
         lds_barrier();
     }
 
-    for (int it = 0; it < n_it; ++it) {
-        const int buf = it & 1;
-        const T *Qs = Qbuf[buf];
-        const T *Gs = Gbuf[buf];
-        const int q0 = it_q0(it);
-        stage(buf ^ 1);  // iteration it+1 into the free buffers
-        fetch(it + 2);
-
-        // S = Q K^T, dP = dO V^T (register r: query q0 + 8(r/4) + 4hh + r%4, key `key`)
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    // S = Q K^T and dP = dO V^T of the tile in buffer `bf` (register r:
+    // query q0 + 8(r/4) + 4hh + r%4, key `key`)
+    auto sdp = [&](int bf, f32x16_t &s, f32x16_t &dp) {
+        const T *Qs = Qbuf[bf];
+        const T *Gs = Gbuf[bf];
+        s = f32x16_t{};
+        dp = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
             const v8 qa = *reinterpret_cast<const v8 *>(&Qs[c * ST + 16 * t + 8 * hh]);
@@ -393,6 +405,23 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             s = M::mma32(qa, kop[t], s);
             dp = M::mma32(ga, vop[t], dp);
         }
+    };
+    // dV^T += dO^T P,  dK^T += Q^T dS  with the tile in buffer `bf`
+    auto dkdv = [&](int bf, const v8 (&pop)[2], const v8 (&dsop)[2]) {
+        const T *Qs = Qbuf[bf];
+        const T *Gs = Gbuf[bf];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) {
+                accv[mb] = M::mma32(tr_operand<T, ST>(Gs, tr_off, mb, t), pop[t], accv[mb]);
+                acck[mb] = M::mma32(tr_operand<T, ST>(Qs, tr_off, mb, t), dsop[t], acck[mb]);
+            }
+    };
+    // P and dS of iteration it from its S and dP, packed as MFMA operands
+    auto pds = [&](int it, const f32x16_t &s, const f32x16_t &dp, v8 (&pop)[2], v8 (&dsop)[2]) {
+        const int bf = it & 3;
+        const int q0 = it_q0(it);
         f32x16_t p, ds;
         // Tiles where every query sees every key of the wave (uniform test)
         // skip the per-element mask.
@@ -400,8 +429,8 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         if (full) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[buf][8 * i + 4 * hh]);
-                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[buf][8 * i + 4 * hh]);
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[bf][8 * i + 4 * hh]);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[bf][8 * i + 4 * hh]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * i + e;
@@ -413,8 +442,8 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[buf][8 * i + 4 * hh]);
-                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[buf][8 * i + 4 * hh]);
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&Lbuf[bf][8 * i + 4 * hh]);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&Dbuf[bf][8 * i + 4 * hh]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * i + e;
@@ -426,18 +455,44 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                 }
             }
         }
-        // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const v8 pop = pack_block<T>(p, t);
-            const v8 dsop = pack_block<T>(ds, t);
-#pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb) {
-                accv[mb] = M::mma32(tr_operand<T, ST>(Gs, tr_off, mb, t), pop, accv[mb]);
-                acck[mb] = M::mma32(tr_operand<T, ST>(Qs, tr_off, mb, t), dsop, acck[mb]);
-            }
+            pop[t] = pack_block<T>(p, t);
+            dsop[t] = pack_block<T>(ds, t);
         }
+    };
+
+    f32x16_t s_a, dp_a, s_b, dp_b;
+    v8 p_a[2], ds_a[2], p_b[2], ds_b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        p_a[t] = bitcast<v8>(u32x4_t{0u, 0u, 0u, 0u});
+        ds_a[t] = p_a[t];
+    }
+    if (n_it > 0) sdp(0, s_a, dp_a);
+
+    // One step.  On entry: (sc, dpc) = S, dP of iteration it; (pp, dsp) =
+    // operands of iteration it-1; buffers (it-1..it+1) % 4 staged; the
+    // registers hold iteration it+2.
+    auto step = [&](int it, f32x16_t &sc, f32x16_t &dpc, f32x16_t &sn, f32x16_t &dpn,
+                    const v8 (&pp)[2], const v8 (&dsp)[2], v8 (&pc)[2], v8 (&dsc)[2]) {
+        stage((it + 2) & 3);  // last read (iteration it-2's dV/dK) before the previous barrier
+        fetch(it + 3);
+        sdp((it + 1) & 3, sn, dpn);
+        dkdv((it + 3) & 3, pp, dsp);  // iteration it-1
+        pds(it, sc, dpc, pc, dsc);
         lds_barrier();
+    };
+    int it = 0;
+    for (; it + 1 < n_it; it += 2) {
+        step(it, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
+        step(it + 1, s_b, dp_b, s_a, dp_a, p_b, ds_b, p_a, ds_a);
+    }
+    if (it < n_it) {
+        step(it, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
+        dkdv(it & 3, p_b, ds_b);  // the last iteration's deferred products
+    } else if (n_it > 0) {
+        dkdv((n_it - 1) & 3, p_a, ds_a);
     }
 
     if (key < Nk) {
