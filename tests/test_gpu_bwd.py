@@ -109,6 +109,17 @@ def test_dtypes_and_head_dims(dt, d):
     run_bwd(2, 4, 2, 250, 250, d, dt, True, seed=d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv,N", [(2, 2, 129), (3, 1, 161), (6, 2, 97)])
+def test_pipeline_iteration_counts(d, H, Hkv, N):
+    """The dK/dV sweep is software-pipelined over (query head, query tile)
+    iterations: odd and even counts, a single iteration (causal N = 129 with
+    one query head per KV head: the last key block sees one query tile) and
+    GQA groups of 1, 2 and 3, causal and full."""
+    run_bwd(1, H, Hkv, N, N, d, "bf16", True, seed=N + d)
+    run_bwd(1, H, Hkv, N, N, d, "f16", False, seed=N + d + 1)
+
+
 def test_gpt2_shape_heads_causal():
     """GPT-2-small-shaped heads (d = 64) at N = 2048, causal, bf16."""
     run_bwd(2, 4, 2, 2048, 2048, 64, "bf16", True, seed=5)
