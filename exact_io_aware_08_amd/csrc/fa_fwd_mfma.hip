@@ -68,12 +68,17 @@ template <> struct Pack2<__bf16> {
     static __device__ __forceinline__ float add(v2, float p0, float p1, float c) {
         return c + p0 + p1;
     }
+    // the first pair of a sum (p0 >= 0, so this equals 0 + p0 + p1)
+    static __device__ __forceinline__ float first(v2, float p0, float p1) { return p0 + p1; }
 };
 template <> struct Pack2<_Float16> {
     typedef _Float16 v2 __attribute__((ext_vector_type(2)));
     static __device__ __forceinline__ float add(v2 a, float, float, float c) {
         const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
         return __builtin_amdgcn_fdot2(a, one, c, false);
+    }
+    static __device__ __forceinline__ float first(v2 a, float p0, float p1) {
+        return add(a, p0, p1, 0.f);
     }
 };
 
@@ -245,11 +250,16 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 #pragma unroll
         for (int i = 0; i < DW / 32; ++i) acc[qb][i] = f32x16_t{};
     float m_ref[QB], l_run[QB];  // reference max (raw units; same in lanes l, l^32), row-sum share
+    float mneg[QB];              // -m_ref * scale * log2(e), 0 while m_ref = -inf
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_ref[qb] = -INFINITY;
         l_run[qb] = 0.f;
+        mneg[qb] = 0.f;
     }
+    auto set_mneg = [&](int qb) {
+        mneg[qb] = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb] * scale_log2;
+    };
 
     const KvMap<D, QB> mp(tid, (int)sizeof(T));
     // Transpose-read address of this lane within a V tile: 16-lane group
@@ -336,9 +346,13 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // so the only waits on global loads are for data requested a full tile
     // earlier.  Tiles past a wave's causal limit are processed fully masked
     // (weight 0), which keeps the hot block free of branches.
-    auto step = [&](int j, int vb, f32x16_t (&sc)[NSB], f32x16_t (&sn)[NSB], const v8 (&pp)[NSB][2],
+    // The three V buffers rotate through element offsets held in scalar
+    // registers: vo_prev = V_{j-1}, vo_cur = V_j, vo_next = V_{j+1} at step j.
+    constexpr int VSZ = BC * VS;
+    int vo_prev = 2 * VSZ, vo_cur = 0, vo_next = VSZ;
+    T *const Vb0 = &Vbuf[0][0];
+    auto step = [&](int j, f32x16_t (&sc)[NSB], f32x16_t (&sn)[NSB], const v8 (&pp)[NSB][2],
                     v8 (&pc)[NSB][2]) {
-        const int vprev = vb == 0 ? 2 : vb - 1, vnext = vb == 2 ? 0 : vb + 1;
         const int j0 = j * BC;
         if (DS > 1) x_add(j & 1, sc);  // full S^T of tile j
         // ---- mask: ragged last tile, the diagonal band and beyond (causal) ----
@@ -381,6 +395,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             for (int qb = 0; qb < QB; ++qb) {
                 const float m = tile_max(qb);
                 m_ref[qb] = m_ref[qb] == -INFINITY ? m : m_ref[qb];
+                set_mneg(qb);
             }
         }
         // Any row: raise the reference to this tile's max, rescaling what
@@ -393,6 +408,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                 const bool raise = m > m_ref[qb];
                 const float alpha = raise ? fast_exp2((m_ref[qb] - m) * scale_log2) : 1.f;
                 m_ref[qb] = raise ? m : m_ref[qb];
+                set_mneg(qb);
                 l_run[qb] *= alpha;
 #pragma unroll
                 for (int i = 0; i < DW / 32; ++i) acc[qb][i] *= alpha;
@@ -402,12 +418,6 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         // P = exp2(s*c - m*c) packed to 16-bit, with this tile's row sums.
         float ts[QB];
         auto make_p = [&]() {
-            float mneg[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                mneg[qb] = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb] * scale_log2;
-                ts[qb] = 0.f;
-            }
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -423,7 +433,8 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
                         // sinks all of them past the range-check branch below,
                         // out of the MFMA-interleaved block
                         asm volatile("" : "+v"(pk[e]));
-                        ts[qb] = P2::add(pk[e], p0, p1, ts[qb]);
+                        if (sb % NKB == 0 && t == 0 && e == 0) ts[qb] = P2::first(pk[e], p0, p1);
+                        else ts[qb] = P2::add(pk[e], p0, p1, ts[qb]);
                     }
                     pc[sb][t] = bitcast<v8>(u32x4_t{bitcast<uint32_t>(pk[0]), bitcast<uint32_t>(pk[1]),
                                                     bitcast<uint32_t>(pk[2]), bitcast<uint32_t>(pk[3])});
@@ -438,7 +449,7 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         //      the trading-day prefill) ----
         __builtin_amdgcn_s_setprio(1);
         scores<T, D, QB>(Kbuf[(j + 1) & 1], qop, c, hh, dbase, sn);
-        pv(Vbuf[vprev], pp);
+        pv(Vb0 + vo_prev, pp);
         make_p();
         constexpr int N_MFMA = NSB * DW / 8;
         __builtin_amdgcn_sched_group_barrier(0x0100, NKB * (DW / 16) + 2 * (DW / 32) * NKB * 2, 0);  // LDS reads
@@ -465,27 +476,32 @@ fwd_mfma_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
         // ---- staging of the next tiles into buffers not read in this step ----
         store_rows<T, D, QB>(Kbuf[j & 1], mp.kst, kreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Kb, Nk, tile(j + 3)), mp, kreg);
-        store_rows<T, D, QB>(Vbuf[vnext], mp.vst, vreg);
+        store_rows<T, D, QB>(Vb0 + vo_next, mp.vst, vreg);
         load_rows<T, D, QB>(rows_rsrc<T, D>(Vb, Nk, tile(j + 2)), mp, vreg);
         lds_barrier();
     };
 
     // Unrolled by two so the score and P registers swap roles instead of
     // being copied.
-    int vb = 0;  // j % 3
+    auto rotate = [&]() {
+        const int t = vo_prev;
+        vo_prev = vo_cur;
+        vo_cur = vo_next;
+        vo_next = t;
+    };
     for (int j = 0; j < nkt; j += 2) {
-        step(j, vb, s_a, s_b, p_a, p_b);
-        vb = vb == 2 ? 0 : vb + 1;
+        step(j, s_a, s_b, p_a, p_b);
+        rotate();
         if (j + 1 < nkt) {
-            step(j + 1, vb, s_b, s_a, p_b, p_a);
-            vb = vb == 2 ? 0 : vb + 1;
+            step(j + 1, s_b, s_a, p_b, p_a);
+            rotate();
         }
     }
-    // the deferred P V of the last tile (V of tile nkt-1 is in Vbuf[(nkt-1)%3])
+    // the deferred P V of the last tile (after the last rotation vo_prev
+    // holds V of tile nkt-1)
     if (nkt > 0) {
-        const int vlast = vb == 0 ? 2 : vb - 1;
-        if (nkt & 1) pv(Vbuf[vlast], p_b);
-        else pv(Vbuf[vlast], p_a);
+        if (nkt & 1) pv(Vb0 + vo_prev, p_b);
+        else pv(Vb0 + vo_prev, p_a);
     }
 
     // ---- epilogue: O = acc / l, LSE = m*scale + ln l ----
