@@ -209,7 +209,7 @@ def main():
            "data": "synthetic"}
 
     # ---------------- prefill: the step ----------------
-    c3 = fagen.CONFIGS[3]
+    c3 = fagen.WORKLOADS["trading_day_prefill_bf16"]
     B, H, N, d = c3["B"], c3["H"], c3["Nq"], c3["d"]
     q3n, k3n, v3n = fagen.make_inputs(c3, 0)
     q3, k3, v3 = to_dev(q3n, "bf16"), to_dev(k3n, "bf16"), to_dev(v3n, "bf16")
@@ -235,7 +235,7 @@ def main():
 
     # ---------------- decode ----------------
     if args.only in ("all", "decode"):
-        c4 = fagen.CONFIGS[4]
+        c4 = fagen.WORKLOADS["gqa_decode_bf16"]
         B4, H4, Hkv4, Nk4, d4 = c4["B"], c4["H"], c4["Hkv"], c4["Nk"], c4["d"]
         q4n, k4n, v4n = fagen.make_inputs(c4, 0)
         q4 = to_dev(q4n, "bf16")
@@ -298,14 +298,14 @@ def main():
     if args.only == "all" and not args.no_extra:
         extra = {}
         # tiny exact fp32 check (launch-bound)
-        c1 = fagen.CONFIGS[1]
+        c1 = fagen.WORKLOADS["tiny_exact_f32"]
         q1n, k1n, v1n = fagen.make_inputs(c1, 0)
         q1, k1, v1 = (to_dev(x, "f32") for x in (q1n, k1n, v1n))
         ms1 = _timed(lambda i: fa.fwd(q1, k1, v1, causal=False, scale=c1["scale"]), 200, 50, torch)
         extra["tiny_exact_f32"] = {"us_per_call": round(ms1 * 1e3, 2), "shape": [1, 1, 256, 64],
                                    "causal": False}
         # GPT-2-small-shaped prefill
-        c2 = fagen.CONFIGS[2]
+        c2 = fagen.WORKLOADS["gpt2s_prefill_bf16"]
         q2n, k2n, v2n = fagen.make_inputs(c2, 0)
         q2, k2, v2 = (to_dev(x, "bf16") for x in (q2n, k2n, v2n))
         o2 = torch.empty_like(q2)
@@ -379,7 +379,7 @@ def main():
             "note": "E4M3 Q, K, V and P (S = 256), running max per 64-key tile; bf16 O"}
         del q8, k8, v8, o8, l8
         # P-cast on the attention-sink workload: flush counters and time per run
-        c5 = fagen.CONFIGS[5]
+        c5 = fagen.WORKLOADS["pcast_sink_f32"]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
         q5n, k5n, v5n = fagen.sink_inputs(0, B5, H5, N5, d5, 0.0)
         q5, v5 = to_dev(q5n, "f32"), to_dev(v5n, "f32")
@@ -442,8 +442,9 @@ def main():
                                          f"optimised CPU baseline"}
         # the other workloads in full, on the same oracle (seconds, visible pairs per second)
         others = {}
-        for ci, causal_i in ((1, False), (2, True), (4, False)):
-            cf = fagen.CONFIGS[ci]
+        for wname, causal_i in (("tiny_exact_f32", False), ("gpt2s_prefill_bf16", True),
+                                ("gqa_decode_bf16", False)):
+            cf = fagen.WORKLOADS[wname]
             xs = [fagen.storage_to_f32(x, cf["dtype"]) for x in fagen.make_inputs(cf, 0)]
             t0 = time.perf_counter()
             oracle.attention(*xs, causal_i, float(np.float32(1.0 / math.sqrt(cf["d"]))), nthreads=threads)
@@ -458,7 +459,7 @@ def main():
         # F(Delta, S) and MSE against exact attention on sampled rows
         import oracle
         d4 = oracle.expected_max_gauss(4)
-        c5 = fagen.CONFIGS[5]
+        c5 = fagen.WORKLOADS["pcast_sink_f32"]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
         rows5 = np.stack([fagen.sample_rows(1, h, N5, 8) for h in range(H5)])
         q5n, k5n, v5n = fagen.sink_inputs(0, B5, H5, N5, d5, 0.0)

@@ -31,7 +31,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "stream_key", "uniform", "normal", "to_storage", "iid_normal",
+    "WORKLOADS", "stream_key", "uniform", "normal", "to_storage", "iid_normal",
     "ar1_series", "sink_inputs", "make_inputs", "sample_rows", "outlier_normal", "random_signs",
 ]
 
@@ -180,25 +180,25 @@ def random_signs(seed: int, d: int) -> np.ndarray:
 
 
 # Workload table.  'scale' is the fp32 value of 1/sqrt(d).
-CONFIGS = {
-    1: dict(name="tiny_exact_f32", B=1, H=1, Hkv=1, Nq=256, Nk=256, d=64,
+WORKLOADS = {
+    "tiny_exact_f32": dict(name="tiny_exact_f32", B=1, H=1, Hkv=1, Nq=256, Nk=256, d=64,
             dtype="f32", causal=False, kind="iid"),
-    2: dict(name="gpt2s_prefill_bf16", B=4, H=12, Hkv=12, Nq=2048, Nk=2048, d=64,
+    "gpt2s_prefill_bf16": dict(name="gpt2s_prefill_bf16", B=4, H=12, Hkv=12, Nq=2048, Nk=2048, d=64,
             dtype="bf16", causal=True, kind="iid"),
-    3: dict(name="trading_day_prefill_bf16", B=1, H=12, Hkv=12, Nq=23400, Nk=23400,
+    "trading_day_prefill_bf16": dict(name="trading_day_prefill_bf16", B=1, H=12, Hkv=12, Nq=23400, Nk=23400,
             d=64, dtype="bf16", causal=True, kind="ar1", sample_rows=512),
-    4: dict(name="gqa_decode_bf16", B=16, H=32, Hkv=4, Nq=1, Nk=8192, d=64,
+    "gqa_decode_bf16": dict(name="gqa_decode_bf16", B=16, H=32, Hkv=4, Nq=1, Nk=8192, d=64,
             dtype="bf16", causal=False, kind="iid", decode=True),
-    5: dict(name="pcast_sink_f32", B=1, H=32, Hkv=32, Nq=8192, Nk=8192, d=128,
+    "pcast_sink_f32": dict(name="pcast_sink_f32", B=1, H=32, Hkv=32, Nq=8192, Nk=8192, d=128,
             dtype="f32", causal=True, kind="sink", deltas=(4.0, 6.0, 8.0, 10.0),
             n_sink=4),
 }
-for _c in CONFIGS.values():
+for _c in WORKLOADS.values():
     _c["scale"] = float(np.float32(1.0 / math.sqrt(_c["d"])))
 
 
 def make_inputs(cfg: dict, seed: int = 0, delta: float | None = None):
-    """Q, K, V storage arrays for a workload dict (see CONFIGS)."""
+    """Q, K, V storage arrays for a workload dict (see WORKLOADS)."""
     B, H, Hkv, Nq, Nk, d = (cfg[k] for k in ("B", "H", "Hkv", "Nq", "Nk", "d"))
     dt = cfg["dtype"]
     kind = cfg.get("kind", "iid")

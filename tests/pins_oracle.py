@@ -447,7 +447,7 @@ def pin_trading_day_workload():
     an fp16 score matrix of about 12.9 GB -- the full-size prefill shape."""
     import fagen
     g = golden("trading_day.txt")
-    c3 = fagen.CONFIGS[3]
+    c3 = fagen.WORKLOADS["trading_day_prefill_bf16"]
     assert c3["Nq"] == c3["Nk"] == g["steps_per_day"] == 6.5 * 3600 and c3["H"] == g["heads"]
     gb = g["steps_per_day"] ** 2 * g["heads"] * 2 / 1e9
     assert abs(gb - g["score_matrix_gb_printed"]) / g["score_matrix_gb_printed"] < 0.10

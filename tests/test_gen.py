@@ -68,12 +68,15 @@ def test_sample_rows():
     assert np.array_equal(fagen.sample_rows(0, 0, 10, 512), np.arange(10))
 
 
-def test_config_table():
-    c = fagen.CONFIGS
-    assert (c[3]["Nq"], c[3]["H"], c[3]["d"], c[3]["dtype"]) == (23400, 12, 64, "bf16")
-    assert (c[4]["B"], c[4]["H"], c[4]["Hkv"], c[4]["Nk"]) == (16, 32, 4, 8192)
-    assert c[1]["scale"] == 0.125 and c[5]["scale"] == float(np.float32(1 / math.sqrt(128)))
-    q, k, v = fagen.make_inputs(c[1], 0)
+def test_workload_table():
+    c = fagen.WORKLOADS
+    td, dec, tiny = c["trading_day_prefill_bf16"], c["gqa_decode_bf16"], c["tiny_exact_f32"]
+    assert (td["Nq"], td["H"], td["d"], td["dtype"]) == (23400, 12, 64, "bf16")
+    assert (dec["B"], dec["H"], dec["Hkv"], dec["Nk"]) == (16, 32, 4, 8192)
+    assert tiny["scale"] == 0.125
+    assert c["pcast_sink_f32"]["scale"] == float(np.float32(1 / math.sqrt(128)))
+    assert all(name == w["name"] for name, w in c.items())
+    q, k, v = fagen.make_inputs(tiny, 0)
     assert q.dtype == np.float32 and q.shape == (1, 1, 256, 64)
-    q2, _, _ = fagen.make_inputs(c[1], 0)
+    q2, _, _ = fagen.make_inputs(tiny, 0)
     assert np.array_equal(q, q2)

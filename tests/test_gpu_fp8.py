@@ -207,7 +207,7 @@ def test_fp8_trading_day_shape_sampled_rows():
     every head against the emulation, codes of the GPU quantiser against the
     oracle's on the whole tensors."""
     need_gpu()
-    c = fagen.CONFIGS[3]
+    c = fagen.WORKLOADS["trading_day_prefill_bf16"]
     B, H, N, d = c["B"], c["H"], c["Nq"], c["d"]
     announce(f"fa_fwd_fp8 trading-day shape B={B} H={H} N={N}")
     q, k, v = (widen(x, "bf16") for x in fagen.make_inputs(c, 0))

@@ -44,7 +44,7 @@ def run_case(B, H, Hkv, Nq, Nk, d, dt, causal, seed=0, kind="iid", rows=None, sc
 
 def test_tiny_exact_f32():
     """256 x 64 fp32, full attention, seed 0."""
-    c = fagen.CONFIGS[1]
+    c = fagen.WORKLOADS["tiny_exact_f32"]
     m = run_case(1, 1, 1, 256, 256, 64, "f32", False, scale=c["scale"])
     assert m["max_abs"] <= 1e-5
 

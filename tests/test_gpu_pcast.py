@@ -93,7 +93,7 @@ def _model_flush(delta, S, n=400_000):
 def test_pcast_sink_workload_full_size(delta):
     """B=1, H=32, N=8192, d=128, causal, sink keys 0..3 shifted by Delta."""
     need_gpu()
-    c = fagen.CONFIGS[5]
+    c = fagen.WORKLOADS["pcast_sink_f32"]
     B, H, N, d = c["B"], c["H"], c["Nq"], c["d"]
     q, k, v = fagen.sink_inputs(0, B, H, N, d, delta)
     rows = np.stack([np.unique(np.concatenate([[0, N - 1], fagen.sample_rows(0, h, N, 14)]))
