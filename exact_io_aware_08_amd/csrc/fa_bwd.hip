@@ -66,7 +66,11 @@ bwd_dot_kernel(const T *__restrict__ O, const T *__restrict__ dO, float *__restr
 template <int D> struct TileMap {
     static constexpr int CPR = D / 8;
     static constexpr int CH = TK * CPR / 256;  // 16-byte chunks per thread
-    static constexpr int ST = D + 8;           // LDS row stride (elements)
+    // LDS row stride (elements).  Each staged tile is read both as 16-byte
+    // rows and by transpose reads; D + 40 (20 mod 32 dwords) measured best of
+    // D + 8 ... D + 48 for the two together (LDS bank conflicts of D + 8
+    // cost 1-6%).
+    static constexpr int ST = D + 40;
     static_assert(CH >= 1 && CH * 256 == TK * CPR, "tile staging split");
     int off[CH], lds[CH];
     __device__ __forceinline__ TileMap(int tid, int elem_bytes) {
