@@ -333,8 +333,20 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     }
     const int nqt = nqt_all - qt0;      // tiles per head
     const int n_it = nqt * G;           // iterations: (head in group, query tile)
-    auto it_head = [&](int it) { return hk * G + it / max(nqt, 1); };
-    auto it_q0 = [&](int it) { return (qt0 + it % max(nqt, 1)) * TK; };
+    // Iteration it covers query head hk * G + it / nqt and query tile
+    // qt0 + it % nqt.  The loads and the P/dS work each walk the iterations
+    // in order, so each keeps its own (head, tile) position and advances it
+    // by one (no integer division in the loop).
+    struct ItPos {
+        int it, h, qt;
+    };
+    auto advance = [&](ItPos &ps) {
+        ++ps.it;
+        if (++ps.qt == nqt_all) {
+            ps.qt = qt0;
+            ++ps.h;
+        }
+    };
 
     f32x16_t acck[D / 32], accv[D / 32];
 #pragma unroll
@@ -347,31 +359,28 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     const int tr_off = (4 * hh + ((lane & 15) >> 2)) * ST + 16 * (c >> 4) + 4 * (lane & 3);
     u32x4_t qreg[TM::CH], greg[TM::CH];
     float lreg = 0.f;  // threads 0..31: LSE of row tid; 32..63: D of row tid-32
-    auto fetch = [&](int it) {  // global -> registers for iteration it (clamped)
-        const int itc = min(it, n_it - 1);
-        const int hq = it_head(itc), q0 = it_q0(itc);
+    // Global -> registers for the next iteration in order (it stays at the
+    // last iteration once reached).  The LSE is kept raw here and converted
+    // when staged: using it at once would make the wave wait for these loads
+    // in the same step.
+    ItPos fp{0, 0, qt0};
+    auto fetch = [&]() {
+        const int hq = hk * G + fp.h, q0 = fp.qt * TK;
         const size_t qoff = ((size_t)b * H + hq) * Nq * D;
         load_tile<D>(rows_rsrc<T, D>(Q + qoff, Nq, q0), mp, qreg);
         load_tile<D>(rows_rsrc<T, D>(dO + qoff, Nq, q0), mp, greg);
         if (tid < 2 * TK) {
             const int r = q0 + (tid & (TK - 1));
             const size_t ro = ((size_t)b * H + hq) * Nq + r;
-            if (r < Nq) {
-                if (tid < TK) {
-                    const float l = LSE[ro];
-                    lreg = l == -INFINITY ? 0.f : l * kLog2e;
-                } else {
-                    lreg = Dv[ro];
-                }
-            } else {
-                lreg = 0.f;
-            }
+            lreg = 0.f;
+            if (r < Nq) lreg = tid < TK ? LSE[ro] : Dv[ro];
         }
+        if (fp.it < n_it - 1) advance(fp);
     };
     auto stage = [&](int buf) {
         store_tile<T, D>(Qbuf[buf], mp, qreg);
         store_tile<T, D>(Gbuf[buf], mp, greg);
-        if (tid < TK) Lbuf[buf][tid] = lreg;
+        if (tid < TK) Lbuf[buf][tid] = lreg == -INFINITY ? 0.f : lreg * kLog2e;
         else if (tid < 2 * TK) Dbuf[buf][tid - TK] = lreg;
     };
 
@@ -383,11 +392,11 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // buffer 3 stands for iteration -1, whose operands are zero, and holds
     // zeros so that its products stay finite.
     if (n_it > 0) {
-        fetch(0);
+        fetch();  // iteration 0
         stage(0);
-        fetch(1);
+        fetch();  // 1
         stage(1);
-        fetch(2);
+        fetch();  // 2
         for (int i = tid; i < TK * ST / 8; i += 256) {
             reinterpret_cast<u32x4_t *>(Qbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
             reinterpret_cast<u32x4_t *>(Gbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -423,9 +432,11 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
             }
     };
     // P and dS of iteration it from its S and dP, packed as MFMA operands
+    ItPos pq{0, 0, qt0};  // the iteration whose P and dS the next step forms
     auto pds = [&](int it, const f32x16_t &s, const f32x16_t &dp, v8 (&pop)[2], v8 (&dsop)[2]) {
         const int bf = it & 3;
-        const int q0 = it_q0(it);
+        const int q0 = pq.qt * TK;
+        advance(pq);
         f32x16_t p, ds;
         // Tiles where every query sees every key of the wave (uniform test)
         // skip the per-element mask.
@@ -481,7 +492,7 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     auto step = [&](int it, f32x16_t &sc, f32x16_t &dpc, f32x16_t &sn, f32x16_t &dpn,
                     const v8 (&pp)[2], const v8 (&dsp)[2], v8 (&pc)[2], v8 (&dsc)[2]) {
         stage((it + 2) & 3);  // last read (iteration it-2's dV/dK) before the previous barrier
-        fetch(it + 3);
+        fetch();              // iteration it+3
         sdp((it + 1) & 3, sn, dpn);
         dkdv((it + 3) & 3, pp, dsp);  // iteration it-1
         pds(it, sc, dpc, pc, dsc);
