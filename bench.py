@@ -9,12 +9,14 @@ cache (B=16, 32/4 heads, Nk=8192, d=64, bf16), each with its roofline, and
 the fp64 CPU oracle timed on a bounded sample of the prefill rows.
 
 Timing: HIP events on the stream the kernels are launched on (torch's current
-stream), around exactly K calls after W warm-up calls, bracketed by device
-synchronisation.  A spin kernel is queued ahead of the timed region so every
-call is already enqueued when the GPU reaches the first one; host launch
-overhead therefore does not enter the measured time.  Decode rotates over
-four KV caches (4 x 134 MB, more than the 256 MB last-level cache) so each
-call reads its cache from HBM.
+stream), around exactly K back-to-back calls after W warm-up calls, bracketed
+by device synchronisation.  Calls shorter than their host launch cost (decode
+and the small workloads) are queued behind a spin kernel, so host launch
+overhead does not enter their measured time; long calls (the prefill step,
+backward, FP8, P-cast) are not, because the first MFMA-heavy launches after
+an idle spin run slower while the clock settles.  Decode rotates over four KV
+caches (4 x 134 MB, more than the 256 MB last-level cache) so each call reads
+its cache from HBM.
 """
 from __future__ import annotations
 
@@ -172,8 +174,9 @@ def main():
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: sequence-length sweep N in {512, 4096, 32768} "
-                         "(B=1, H=12, d=64, bf16, causal, AR(1) inputs): time and peak device "
-                         "memory of fa_fwd (+ fa_bwd) against materialised attention")
+                         "at d in {64, 128, 256} (B=1, H=12, bf16, causal, AR(1) inputs): time "
+                         "and peak device memory of fa_fwd (+ fa_bwd at d <= 128) against "
+                         "materialised attention")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (tiny fp32, GPT-2-small prefill, P-cast sink)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -182,7 +185,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU; libfa has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
