@@ -129,14 +129,17 @@ def _sweep(torch, fa, fagen, to_dev, dev):
             return r, torch.cuda.max_memory_allocated() - base
 
         it = max(3, min(200, int(2e12 / flops)))
+        qa = flops < 2e11   # queue short calls behind a spin kernel; time long ones without it
+        wu = max(3, int(5e13 / flops))  # about 50 ms of warm-up work: the clock settles
         (o, lse), mem_f = peak(lambda: fa.fwd(q, k, v, causal=True, scale=scale))
-        ms_f = _timed(lambda i: fa.fwd(q, k, v, causal=True, scale=scale), it, 3, torch)
+        ms_f = _timed(lambda i: fa.fwd(q, k, v, causal=True, scale=scale), it, wu, torch, qa)
         row["fa_fwd"] = {"ms": round(ms_f, 4), "tflops": round(flops / (ms_f * 1e-3) / 1e12, 1),
                          "extra_bytes": int(mem_f)}
         g = torch.empty_like(q).normal_(generator=torch.Generator(device=dev).manual_seed(1))
         if d <= 128:
             _, mem_b = peak(lambda: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale))
-            ms_b = _timed(lambda i: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale), it, 3, torch)
+            ms_b = _timed(lambda i: fa.bwd(q, k, v, o, g, lse, causal=True, scale=scale), it, wu, torch,
+                          qa)
             row["fa_bwd"] = {"ms": round(ms_b, 4),
                              "tflops": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 1),
                              "extra_bytes": int(mem_b)}
@@ -151,7 +154,7 @@ def _sweep(torch, fa, fagen, to_dev, dev):
             return torch.matmul(torch.softmax(sc, dim=-1), v)
 
         om, mem_m = peak(materialised)
-        ms_m = _timed(lambda i: materialised(), max(3, it // 4), 2, torch)
+        ms_m = _timed(lambda i: materialised(), max(3, it // 4), 2, torch, qa)
         row["materialised_fwd"] = {"ms": round(ms_m, 4), "extra_bytes": int(mem_m),
                                    "max_abs_diff_vs_fa_fwd": float((om.float() - o.float()).abs().max())}
         row["fwd_speedup"] = round(ms_m / ms_f, 2)
