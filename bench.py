@@ -440,6 +440,13 @@ def main():
                          "lse_max_abs": float(np.abs(lg - l_ref[0]).max()),
                          "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3
                                     and np.abs(lg - l_ref[0]).max() <= 1e-3)}
+        if not out["parity"]["ok"]:
+            # a throughput whose output does not match the oracle is not reported as one
+            out["status"] = "FAILED: prefill output outside the parity tolerances"
+            out["value_unverified"] = out["value"]
+            out["value"] = None
+            out["roofline"]["achieved"] = None
+            out["roofline"]["frac"] = None
         out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"{rows.shape[1]} of {N} rows per head x {H} heads of the "
