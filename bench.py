@@ -213,6 +213,11 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
+    # the native library every timed call goes through (there is no other path)
+    from exact_io_aware_08_amd import _lib as fa_lib
+    fa.load()
+    out["library"] = {"path": os.path.relpath(fa_lib.LIB_PATH, ROOT), "fa_version": fa.version(),
+                      "device": torch.cuda.get_device_properties(0).gcnArchName}
 
     # ---------------- prefill: the step ----------------
     c3 = fagen.WORKLOADS["trading_day_prefill_bf16"]
