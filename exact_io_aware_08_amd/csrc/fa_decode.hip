@@ -63,10 +63,12 @@ template <int D> struct DecodeGeo {
 
 // Buffer resource over `bytes` bytes starting at `base`; loads past the end
 // read as zero.  Wave-uniform arguments.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, int bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, long long bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                             bytes > 0 ? bytes : 0, kBufferFlags);
+    // clamped to the 31-bit range (a wave reads 32 rows past `base` at most)
+    const long long b = bytes < 0 ? 0 : (bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b,
+                                             kBufferFlags);
 }
 
 // Cache addressing.  Contiguous: [B, Hkv, Nk, D], every sequence Nk keys.
@@ -157,7 +159,7 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     const int nsteps = kend > kbeg ? (kend - kbeg + kDecodeStep - 1) / kDecodeStep : 0;
     auto load_step = [&](int sp, int st) {
         const int rel = st * kDecodeStep + w * WK;  // first key of this wave's 32, in the slice
-        int left = (kend - kbeg - rel) * D * (int)sizeof(T);
+        long long left = (long long)(kend - kbeg - rel) * D * (long long)sizeof(T);
         size_t row0 = (size_t)(kbeg + rel) * D;  // element offset of the block's first key
         if (PAGED) {
             // wave-uniform: one table entry per 32-key block (scalar load)
@@ -166,7 +168,7 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
             const int phys = pc.block_table[(size_t)b * pc.max_pages + pidx];
             const int in_page = t - pidx * pc.page_size;
             const bool ok = t < kend && (unsigned)phys < (unsigned)pc.num_pages;
-            left = ok ? min(kend - t, pc.page_size - in_page) * D * (int)sizeof(T) : 0;
+            left = ok ? (long long)min(kend - t, pc.page_size - in_page) * D * (long long)sizeof(T) : 0;
             row0 = ok ? ((size_t)phys * Hkv + hk) * pc.page_size * D + (size_t)in_page * D : 0;
         }
         const __amdgpu_buffer_rsrc_t rk = span_rsrc(Kb + row0, left);

@@ -105,8 +105,12 @@ constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9
 template <typename T, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int j0)
 {
-    const int left = rows > j0 ? (rows - j0) * D * (int)sizeof(T) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0, left,
+    // 64-bit, then clamped to the 31-bit range: a slice may hold up to 2^31
+    // elements (more bytes than an int), and every load lies within a tile
+    // or two of the rebased start
+    const long long left = rows > j0 ? (long long)(rows - j0) * D * (long long)sizeof(T) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0,
+                                             (int)(left < 0x7fffffffLL ? left : 0x7fffffffLL),
                                              kBufferFlags);
 }
 
