@@ -163,12 +163,18 @@ fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 
     f32x16_t acc[QB][MB];
     float m_run[QB], l_run[QB];  // running max (log2 units, S-free), sum of S*p (this lane's keys)
+    // E4M3 P operand of each query block.  A pair conversion writes half of a
+    // register and keeps the other half, which the second conversion then
+    // overwrites; starting from the previous tile's register (not from zero)
+    // saves a move per register.
+    i32x8_t pop[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[qb][mb] = f32x16_t{};
         m_run[qb] = -INFINITY;
         l_run[qb] = 0.f;
+        pop[qb] = i32x8_t{};
     }
 
     // staging map: chunk ci = tid + 256 r is row ci / CPR, 16 bytes at (ci % CPR) * 16
@@ -279,7 +285,6 @@ fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
             }
             m_run[qb] = mn;
             const float mref = (mn == -INFINITY) ? 0.f : mn - log2S;  // exp2(x c - mref) = S p
-            i32x8_t pop;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const float ck = kb == 0 ? c0 : c1;
@@ -293,13 +298,13 @@ fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                     l_run[qb] += p1;
                     l_run[qb] += p2;
                     l_run[qb] += p3;
-                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[qb][4 * kb + u], false);
                     pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
-                    pop[4 * kb + u] = pk;
+                    pop[qb][4 * kb + u] = pk;
                 }
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[qb][mb] = mma_fp8(vop[mb], pop, acc[qb][mb]);
+            for (int mb = 0; mb < MB; ++mb) acc[qb][mb] = mma_fp8(vop[mb], pop[qb], acc[qb][mb]);
         }
     }
 
