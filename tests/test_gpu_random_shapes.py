@@ -11,8 +11,15 @@ every output in well under a second, and the same tolerances apply
 import numpy as np
 import pytest
 
+import math
+
+import torch
+
+import exact_io_aware_08_amd as fa
+import oracle
+from gpu_util import announce, compare, need_gpu, to_dev, widen
 from test_gpu_bwd import run_bwd
-from test_gpu_decode import run_decode
+from test_gpu_decode import _paged_case, run_decode
 from test_gpu_fwd import run_case
 
 
@@ -74,6 +81,19 @@ def _decode_config(seed):
     return B, H, Hkv, Nk, d, dt, splits
 
 
+def _paged_config(seed):
+    rng = np.random.default_rng(74_000 + seed)
+    dt = str(rng.choice(["bf16", "f16"]))
+    d = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 4, 8, 20]))
+    B = int(rng.integers(1, 7))
+    page_size = int(rng.choice([32, 64, 96, 128, 256]))
+    lens = [0 if rng.random() < 0.15 else int(rng.integers(1, 3000)) for _ in range(B)]
+    splits = int(rng.choice([0, 3, 8]))
+    return B, H, Hkv, d, dt, page_size, lens, splits
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(16))
 def test_random_prefill(seed):
@@ -95,6 +115,34 @@ def test_random_decode(seed):
     run_decode(B, H, Hkv, Nk, d, dt, splits=splits, seed=seed, poison_ws=True)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(8))
+def test_random_paged_decode(seed):
+    """Paged cache over a random page permutation; table entries past each
+    sequence are invalid (-7); the workspace starts as NaN."""
+    need_gpu()
+    B, H, Hkv, d, dt, ps, lens, splits = _paged_config(seed)
+    announce(f"fa_decode_paged random seed={seed} B={B} H={H} Hkv={Hkv} d={d} {dt} "
+             f"page={ps} lens={lens} splits={splits}")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, lens, ps, d, dt, seed=seed)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    ws = fa.decode_workspace(B, H, Hkv, max_pages * ps, d, splits)
+    if ws is not None:
+        ws.fill_(255)
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=scale,
+                             num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
+            continue
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, scale)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, dt, f"paged b={b} L={L}")
+
+
 def test_configs_span_the_factors():
     """The drawn configurations cover every dtype, head dim and mask mode,
     GQA and MHA, Nq < Nk and Nq > Nk, forced and automatic splits (host-only
@@ -112,3 +160,6 @@ def test_configs_span_the_factors():
     assert {c[4] for c in dc} == {64, 128}
     assert 0 in {c[6] for c in dc} and len({c[6] for c in dc}) >= 3
     assert any(c[1] // c[2] > 16 for c in dc)
+    pg = [_paged_config(s) for s in range(8)]
+    assert {c[5] for c in pg} >= {32, 96} and any(0 in c[6] for c in pg)
+    assert {c[7] for c in pg} == {0, 3, 8} and {c[3] for c in pg} == {64, 128}
