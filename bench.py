@@ -283,13 +283,14 @@ def main():
                 y[perm.to(dev)] = x
                 return y
             pcaches.append((pages(kc), pages(vc)))
-        paged = {"page_size": ps}
+        paged = {"page_size": ps, "splits": "automatic (from the lengths, on the device)"}
+        pws = fa.decode_paged_workspace(B4, H4, Hkv4, npg, ps, d4, device=dev)
         lens_full = torch.full((B4,), Nk4, dtype=torch.int32, device=dev)
         lens_rag = torch.randint(1, Nk4 + 1, (B4,), generator=gen, dtype=torch.int32)
         for name, lens in (("full", lens_full), ("ragged", lens_rag.to(dev))):
             pus = 1e3 * _timed(lambda i: fa.decode_paged(q4, pcaches[i % 4][0], pcaches[i % 4][1],
                                                          table, lens, scale=c4["scale"],
-                                                         workspace=ws, out=o4, lse=l4),
+                                                         workspace=pws, out=o4, lse=l4),
                                args.decode_steps, 400, torch)
             kv_keys = int(lens.sum().item())
             pbytes = 2 * Hkv4 * kv_keys * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4

@@ -19,7 +19,7 @@ import torch
 from ._lib import FA_BF16, FA_F16, FA_F32, FaError, check, load
 
 __all__ = ["fwd", "fwd_pcast", "decode", "cast_e4m3", "kv_tile", "decode_splits",
-           "decode_workspace_bytes", "version", "FaError", "load"]
+           "decode_workspace_bytes", "decode_paged_workspace_bytes", "version", "FaError", "load"]
 
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
@@ -102,6 +102,18 @@ def decode_splits(B: int, H: int, Hkv: int, Nk: int, num_splits: int = 0) -> int
 
 def decode_workspace_bytes(B: int, H: int, Hkv: int, Nk: int, d: int, num_splits: int = 0) -> int:
     return int(load().fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits))
+
+
+def decode_paged_workspace_bytes(B: int, H: int, Hkv: int, max_pages: int, page_size: int, d: int,
+                                 num_splits: int = 0) -> int:
+    return int(load().fa_decode_paged_workspace_bytes(B, H, Hkv, max_pages, page_size, d, num_splits))
+
+
+def decode_paged_workspace(B: int, H: int, Hkv: int, max_pages: int, page_size: int, d: int,
+                           num_splits: int = 0, device="cuda"):
+    """A paged-decode workspace (uint8 tensor), or None when the call needs none."""
+    need = decode_paged_workspace_bytes(B, H, Hkv, max_pages, page_size, d, num_splits)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
 
 
 def decode_workspace(B: int, H: int, Hkv: int, Nk: int, d: int, num_splits: int = 0,
@@ -188,7 +200,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = decode_workspace(B, H, Hkv, max_pages * page_size, d, num_splits, q.device)
+        workspace = decode_paged_workspace(B, H, Hkv, max_pages, page_size, d, num_splits, q.device)
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)

@@ -33,6 +33,7 @@ SIGNATURES = {
     "fa_kv_tile": (_i, [_i, _i, _i]),
     "fa_decode_splits": (_i, [_i, _i, _i, _i, _i]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
     "fa_cast_e4m3": (_i, [_vp, _vp, _vp, _sz, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),

@@ -101,22 +101,27 @@ int decode_chunk(int Nk, int splits, int d)
     return ch < gran ? (int)gran : (int)ch;
 }
 
-// Decode workspace: [per-split LSE | per-split O], the second part starting
-// on a 256-byte boundary.  No workspace without a split.
+// Decode workspace: [per-split LSE | per-split O | per-sequence split
+// counts (automatic paged splits only)], each part starting on a 256-byte
+// boundary.  No workspace without a split.
 struct DecodeLayout {
-    size_t lse_off, o_off, total;
+    size_t lse_off, o_off, cnt_off, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodeLayout decode_layout(int B, int H, int Hkv, int d, int splits)
+DecodeLayout decode_layout(int B, int H, int Hkv, int d, int splits, bool counts = false)
 {
-    DecodeLayout L{0, 0, 0};
+    DecodeLayout L{0, 0, 0, 0};
     if (splits <= 1) return L;
     const size_t rows = (size_t)B * H * splits;
     L.lse_off = 0;
     L.o_off = round256(rows * sizeof(float));
     L.total = L.o_off + rows * (size_t)d * sizeof(float);
+    if (counts) {
+        L.cnt_off = round256(L.total);
+        L.total = L.cnt_off + (size_t)B * sizeof(int);
+    }
     return L;
 }
 
@@ -244,11 +249,14 @@ fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_page
         return FA_ERR_ALIGN;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
-    const int splits = fa_decode_splits(B, H, Hkv, (int)max_seq, num_splits);
-    const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits);
+    const int hq = Hkv * ((H / Hkv + 15) / 16);  // workgroups per (sequence, split)
+    const bool auto_split = num_splits == 0;
+    const int splits = auto_split ? fa::paged_auto_max_splits(max_seq, hq)
+                                  : fa_decode_splits(B, H, Hkv, (int)max_seq, num_splits);
+    const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits, auto_split);
     if (lay.total > 0 && (!workspace || workspace_bytes < lay.total)) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    const long long blocks = (long long)splits * B * Hkv * ((H / Hkv + 15) / 16);
+    const long long blocks = (auto_split ? fa::paged_auto_pairs(B, hq, splits) : (long long)splits * B) * hq;
     if (blocks > kMaxSlice) return FA_ERR_SHAPE;
     if (B == 0) return FA_OK;
     if ((s = device_status()) != FA_OK) return s;
@@ -258,14 +266,29 @@ fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_page
     p.dtype = (int)dtype;
     p.splits = splits;
     p.chunk = decode_chunk((int)max_seq, splits, d);
+    p.auto_split = auto_split ? 1 : 0;
     if (lay.total > 0) {
         char *ws = static_cast<char *>(workspace);
         p.part_lse = reinterpret_cast<float *>(ws + lay.lse_off);
         p.part_o = reinterpret_cast<float *>(ws + lay.o_off);
+        if (auto_split) p.split_counts = reinterpret_cast<int *>(ws + lay.cnt_off);
     }
     p.block_table = block_table; p.seq_lens = seq_lens;
     p.page_size = page_size; p.max_pages = max_pages; p.num_pages = num_pages;
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int H, int Hkv, int max_pages, int page_size, int d,
+                                       int num_splits)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || H % Hkv || max_pages < 1 || page_size < 32 ||
+        num_splits < 0 || num_splits > 4096 || (d != 64 && d != 128))
+        return 0;
+    const long long max_seq = (long long)max_pages * page_size;
+    if (max_seq > kMaxSlice / 128) return 0;
+    if (num_splits > 0) return fa_decode_workspace_bytes(B, H, Hkv, (int)max_seq, d, num_splits);
+    const int hq = Hkv * ((H / Hkv + 15) / 16);
+    return decode_layout(B, H, Hkv, d, fa::paged_auto_max_splits(max_seq, hq), true).total;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq)

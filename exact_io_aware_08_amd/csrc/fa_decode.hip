@@ -82,7 +82,59 @@ struct PagedCache {
     const int *block_table;
     const int *seq_lens;
     int page_size, max_pages, num_pages;
+    int auto_split;     // splits follow the lengths (see paged_auto_pair)
+    int B;              // sequences (entries of seq_lens)
+    int *split_counts;  // automatic splits with a merge: [B], each sequence's split count
 };
+
+// Automatic splits of a paged batch, from the lengths on the device (every
+// wave computes the same values).  The chunk: about kPagedTargetItems
+// workgroups for the whole batch, at least kPagedMinChunk keys, a multiple of
+// the split granularity `gran`, at most the clamp length rounded up (a
+// sequence then has one split).  Sequence b gets
+// min(smax, max(1, ceil(len_b / chunk))) splits, and the (sequence, split)
+// pairs are numbered sequence-major.  Returns the chunk, and for pair p its
+// sequence, split and the sequence's split count; false past the last pair.
+// The first 64 lengths are read once and kept for the scan.
+__device__ bool paged_auto_pair(const int *__restrict__ lens, int B, int cap, int hq, int gran,
+                                int smax, int p, int &chunk, int &b_out, int &sp_out, int &n_out)
+{
+    const int lane = threadIdx.x & 63;
+    const int L0 = lane < B ? min(max(lens[lane], 0), cap) : 0;
+    long long tot = L0;
+    for (int b = lane + 64; b < B; b += 64) tot += min(max(lens[b], 0), cap);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    long long ch = (tot * hq + kPagedTargetItems - 1) / kPagedTargetItems;
+    const long long top = ((long long)cap + gran - 1) / gran * gran;
+    ch = (ch + gran - 1) / gran * gran;
+    ch = ch < top ? ch : top;
+    chunk = (int)(ch > kPagedMinChunk ? ch : kPagedMinChunk);
+
+    int acc = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int b = base + lane;
+        const int L = base == 0 ? L0 : (b < B ? min(max(lens[b], 0), cap) : 0);
+        const int n = b < B ? min(smax, max(1, (L + chunk - 1) / chunk)) : 0;
+        int inc = n;  // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(inc, o);
+            if (lane >= o) inc += t;
+        }
+        const int blk = __shfl(inc, 63);
+        if (p < acc + blk) {
+            const int j = __builtin_ctzll(__ballot(acc + inc > p));
+            const int incj = __shfl(inc, j), nj = __shfl(n, j);
+            b_out = base + j;
+            sp_out = p - (acc + incj - nj);
+            n_out = nj;
+            return true;
+        }
+        acc += blk;
+    }
+    return false;
+}
 
 template <typename T, int D, bool PAGED>
 __global__ void __launch_bounds__(256)
@@ -108,24 +160,47 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     const int lane = tid & 63, c = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int split = (int)(blockIdx.x % (unsigned)splits);
-    const int grp = (int)(blockIdx.x / (unsigned)splits);  // (b, hk, qg)
-    const int qg = grp % n_qgroups;
-    const int bk = grp / n_qgroups;                         // b * Hkv + hk
-    const int hk = bk % Hkv;
-    const int b = bk / Hkv;
+    int split, qg, hk, b, nsp_b = splits;
+    if (PAGED && pc.auto_split) {
+        // workgroup = (pair of the flattened (sequence, split) list, KV head,
+        // query-head group); the chunk follows the batch's total length
+        const int hq = Hkv * n_qgroups;
+        const int cap = pc.max_pages * pc.page_size;
+        const bool found = paged_auto_pair(pc.seq_lens, pc.B, cap, hq, kDecodeStep * Geo::NP, splits,
+                                           (int)(blockIdx.x / (unsigned)hq), chunk, b, split, nsp_b);
+        // the same in every lane and wave: scalar values
+        if (!__builtin_amdgcn_readfirstlane((int)found)) return;  // past the last pair (the grid is an upper bound)
+        chunk = __builtin_amdgcn_readfirstlane(chunk);
+        b = __builtin_amdgcn_readfirstlane(b);
+        split = __builtin_amdgcn_readfirstlane(split);
+        nsp_b = __builtin_amdgcn_readfirstlane(nsp_b);
+        const int r = (int)(blockIdx.x % (unsigned)hq);
+        hk = r / n_qgroups;
+        qg = r - hk * n_qgroups;
+        // one workgroup per sequence tells the merge how many splits it has
+        if (pc.split_counts != nullptr && split == 0 && r == 0 && threadIdx.x == 0)
+            pc.split_counts[b] = nsp_b;
+    } else {
+        split = (int)(blockIdx.x % (unsigned)splits);
+        const int grp = (int)(blockIdx.x / (unsigned)splits);  // (b, hk, qg)
+        qg = grp % n_qgroups;
+        const int bk = grp / n_qgroups;                         // b * Hkv + hk
+        hk = bk % Hkv;
+        b = bk / Hkv;
+    }
     const int h0 = hk * G + qg * 16;
     const int nq = min(16, G - qg * 16);  // real query heads in this group
 
     int nk_b = Nk;
     if (PAGED) nk_b = max(0, min(pc.seq_lens[b], pc.max_pages * pc.page_size));
     const int kbeg = split * chunk;
-    const int kend = min(nk_b, kbeg + chunk);
+    // (automatic splits: the last split of a sequence takes what is left)
+    const int kend = (PAGED && pc.auto_split && split == nsp_b - 1) ? nk_b : min(nk_b, kbeg + chunk);
     // Paged, split: a split wholly past this sequence's length writes nothing
     // (the merge reads only the splits that hold keys); split 0 always writes,
     // so an empty sequence still gets O = 0, LSE = -inf.  Uniform per workgroup.
     if (PAGED && splits > 1 && split > 0 && kbeg >= nk_b) return;
-    const size_t kvoff = PAGED ? 0 : (size_t)bk * Nk * D;
+    const size_t kvoff = PAGED ? 0 : ((size_t)b * Hkv + hk) * Nk * D;
     const T *Kb = K + kvoff;
     const T *Vb = V + kvoff;
 
@@ -340,7 +415,8 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_lse,
                     T *__restrict__ O, float *__restrict__ LSE, int BH, int splits,
-                    const int *__restrict__ seq_lens, int H, int chunk, int cap)
+                    const int *__restrict__ seq_lens, int H, int chunk, int cap,
+                    const int *__restrict__ split_counts)
 {
     constexpr int DPL = D / 64;  // output columns per lane
     constexpr int JB = 16;
@@ -349,7 +425,9 @@ decode_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ 
     if (bh >= BH) return;
     // paged: only the splits that hold keys of this sequence were written
     int nsp = splits;
-    if (seq_lens != nullptr) {
+    if (split_counts != nullptr) {  // automatic splits: as the sweep recorded them
+        nsp = max(1, min(splits, split_counts[bh / H]));
+    } else if (seq_lens != nullptr) {
         const int len = max(0, min(seq_lens[bh / H], cap));
         nsp = max(1, min(splits, (len + chunk - 1) / chunk));
     }
@@ -398,8 +476,12 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
 {
     const int G = p.H / p.Hkv;
     const int n_qgroups = (G + 15) / 16;
-    const unsigned n_blocks = (unsigned)p.splits * (unsigned)(p.B * p.Hkv * n_qgroups);
-    const PagedCache pc{p.block_table, p.seq_lens, p.page_size, p.max_pages, p.num_pages};
+    const int hq = p.Hkv * n_qgroups;
+    const bool auto_split = p.block_table != nullptr && p.auto_split;
+    const unsigned n_blocks = auto_split ? (unsigned)(paged_auto_pairs(p.B, hq, p.splits) * hq)
+                                         : (unsigned)p.splits * (unsigned)(p.B * hq);
+    const PagedCache pc{p.block_table, p.seq_lens, p.page_size, p.max_pages, p.num_pages,
+                        auto_split ? 1 : 0, p.B, auto_split ? p.split_counts : nullptr};
     if (p.block_table != nullptr)
         hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(n_blocks), dim3(256), 0, st,
                            static_cast<const T *>(p.q), static_cast<const T *>(p.k),
@@ -418,7 +500,7 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0,
                        st, p.part_o, p.part_lse, static_cast<T *>(p.o), p.lse, BH, p.splits,
                        p.block_table != nullptr ? p.seq_lens : nullptr, p.H, p.chunk,
-                       p.max_pages * p.page_size);
+                       p.max_pages * p.page_size, auto_split ? p.split_counts : nullptr);
     return hipGetLastError();
 }
 

@@ -33,10 +33,12 @@ struct DecodeProblem {
     int B, H, Hkv, Nk, d;
     float scale;
     int dtype;
-    int splits;  // resolved (>= 1)
-    int chunk;   // keys per split, multiple of decode_chunk_keys(d)
+    int splits;  // resolved (>= 1); with auto_split, the most splits a sequence can get
+    int chunk;   // keys per split, multiple of decode_chunk_keys(d) (not used with auto_split)
+    int auto_split;  // paged cache, automatic splits: the chunk follows the batch's total length
     float *part_o;    // [B, H, splits, d]  (splits > 1)
     float *part_lse;  // [B, H, splits]     (splits > 1)
+    int *split_counts;  // [B] (automatic paged splits with splits > 1)
     // paged cache (block_table == nullptr: contiguous [B, Hkv, Nk, d])
     const int *block_table;  // [B, max_pages]
     const int *seq_lens;     // [B]
@@ -82,6 +84,31 @@ struct Fp8Problem {
 // Tile constants shared by the launchers and fa_kv_tile().
 constexpr int kFwdQTile = 128;     // fewest queries per forward workgroup (grid-size bound)
 constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 32)
+
+// Paged decode with automatic splits.  The kernels read the sequence lengths
+// on the device and cut every sequence into chunks of
+//   chunk = max(kPagedMinChunk, ceil(total_keys * hq / kPagedTargetItems)),
+// rounded up to decode_chunk_keys(d), where hq is the number of workgroups
+// per (sequence, split) pair (KV heads x query-head groups): about
+// kPagedTargetItems workgroups in all, whatever the lengths.  Sequence b gets
+// max(1, ceil(len_b / chunk)) splits, never more than paged_auto_max_splits()
+// (chunk >= kPagedMinChunk and chunk >= len_b * hq / kPagedTargetItems), and
+// the pairs never number more than ceil(kPagedTargetItems / hq) + B.
+constexpr int kPagedTargetItems = 256;
+constexpr int kPagedMinChunk = 512;
+inline int paged_auto_max_splits(long long max_seq, int hq)
+{
+    const long long by_len = (max_seq + kPagedMinChunk - 1) / kPagedMinChunk;
+    const long long by_items = (kPagedTargetItems + hq - 1) / hq;
+    const long long s = by_len < by_items ? by_len : by_items;
+    return s < 1 ? 1 : (int)s;
+}
+inline long long paged_auto_pairs(int B, int hq, int smax)
+{
+    const long long a = (long long)smax * B;
+    const long long b = (kPagedTargetItems + hq - 1) / hq + (long long)B;
+    return a < b ? a : b;
+}
 
 int fwd_f32_kv_tile(int d);   // keys per KV tile, fp32 / P-cast kernel
 int fwd_mfma_kv_tile(int d, long long B, long long H, long long Nq);  // keys per KV tile, bf16 / fp16 kernel

@@ -182,10 +182,22 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
  *   The device tables are not read on the host: lengths outside the range
  *   are clamped and page indices outside [0, num_pages) read nothing, so a
  *   bad table gives wrong numbers but no out-of-bounds access.
- *   num_splits, workspace: as fa_decode with Nk = max_pages * page_size
- *   (size from fa_decode_workspace_bytes(B, H, Hkv, max_pages * page_size,
- *   d, num_splits)).
+ *   num_splits > 0: every sequence is cut into that many chunks of
+ *     ceil(max_pages * page_size / num_splits) keys (rounded up to the split
+ *     granularity), as fa_decode with Nk = max_pages * page_size; the chunks
+ *     past a sequence's end do no work.
+ *   num_splits = 0 (automatic): the kernels read the lengths on the device
+ *     and size one chunk for the whole batch, about 256 workgroups' worth of
+ *     keys in all (at least 512 keys, a multiple of the split granularity);
+ *     sequence b gets max(1, ceil(seq_lens[b] / chunk)) splits.  A ragged
+ *     batch is then spread over the whole GPU instead of following its
+ *     longest sequence.  No host synchronisation.
+ *   workspace: device memory of at least fa_decode_paged_workspace_bytes(B,
+ *     H, Hkv, max_pages, page_size, d, num_splits) bytes (none when that is
+ *     0), 16-byte aligned; contents on entry do not matter.
  */
+size_t fa_decode_paged_workspace_bytes(int B, int H, int Hkv, int max_pages, int page_size, int d,
+                                       int num_splits);
 fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                           const int *block_table, const int *seq_lens, void *o, float *lse,
                           int B, int H, int Hkv, int num_pages, int page_size, int max_pages,

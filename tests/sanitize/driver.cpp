@@ -85,7 +85,12 @@ int main()
           FA_ERR_DTYPE);
     const int *PI = static_cast<const int *>(P);
     CHECK(fa_decode_paged(P, P, P, PI, PI, P, PF, 2, 8, 2, 16, 128, 8, 64, 0.125f, FA_BF16, 0, P,
-                          fa_decode_workspace_bytes(2, 8, 2, 1024, 64, 0), nullptr) == FA_ERR_DEVICE);
+                          fa_decode_paged_workspace_bytes(2, 8, 2, 8, 128, 64, 0), nullptr) == FA_ERR_DEVICE);
+    // automatic splits need room for more splits than the contiguous default
+    CHECK(fa_decode_paged(P, P, P, PI, PI, P, PF, 2, 8, 2, 16, 128, 8, 64, 0.125f, FA_BF16, 0, P,
+                          fa_decode_workspace_bytes(2, 8, 2, 1024, 64, 0), nullptr) == FA_ERR_WORKSPACE);
+    CHECK(fa_decode_paged(P, P, P, PI, PI, P, PF, 2, 8, 2, 16, 128, 8, 64, 0.125f, FA_BF16, 4, P,
+                          fa_decode_paged_workspace_bytes(2, 8, 2, 8, 128, 64, 4), nullptr) == FA_ERR_DEVICE);
     CHECK(fa_decode_paged(P, P, P, nullptr, PI, P, PF, 2, 8, 2, 16, 128, 8, 64, 0.125f, FA_BF16, 0, P,
                           1 << 20, nullptr) == FA_ERR_NULL);
 
@@ -113,6 +118,8 @@ int main()
         for (int n : big) {
             (void)fa_decode_splits(b, 32, 4, n, 0);
             (void)fa_decode_workspace_bytes(b, 32, 4, n, 64, 0);
+            (void)fa_decode_paged_workspace_bytes(b, 32, 4, n, 32, 64, 0);
+            (void)fa_decode_paged_workspace_bytes(b, 32, 4, n, 1 << 20, 128, 0);
             (void)fa_bwd_workspace_bytes(b, 32, n);
         }
     CHECK(fa_decode_splits(-1, 8, 2, 100, 0) == -1 && fa_decode_splits(1, 8, 3, 100, 0) == -1);

@@ -207,10 +207,30 @@ def _paged(**kw):
     (dict(bt=0x10002), "FA_ERR_ALIGN"), (dict(o=PM), "FA_ERR_ALIGN"),
     (dict(dtype=F32), "FA_ERR_DTYPE"), (dict(H=6, Hkv=4), "FA_ERR_GQA"), (dict(d=96), "FA_ERR_HEADDIM"),
     (dict(splits=2, ws=None, ws_bytes=0), "FA_ERR_WORKSPACE"), (dict(B=-2), "FA_ERR_SHAPE"),
+    (dict(max_pages=64, ws_bytes=1000), "FA_ERR_WORKSPACE"),   # automatic splits: 33,288 bytes needed
     (dict(B=0), "FA_OK"),
 ])
 def test_decode_paged_validation(kw, expect):
     assert _paged(**kw) == S[expect]
+
+
+def test_paged_workspace_sizes():
+    """Forced splits: the contiguous decode's layout at Nk = max_pages * page_size.
+    Automatic: room for min(ceil(max_seq / 512), ceil(256 / hq)) splits per
+    sequence, hq = Hkv * ceil((H / Hkv) / 16) workgroups per (sequence, split),
+    then one int per sequence (its split count) on a 256-byte boundary."""
+    assert fa.decode_paged_workspace_bytes(16, 32, 4, 64, 128, 64, 4) == \
+        fa.decode_workspace_bytes(16, 32, 4, 8192, 64, 4)
+    rows = 16 * 32 * 16                      # max_seq 8192 -> 16 splits (hq = 4 allows 64)
+    assert fa.decode_paged_workspace_bytes(16, 32, 4, 64, 128, 64) == rows * 4 + rows * 64 * 4 + 16 * 4
+    rows = 1 * 8 * 32                        # hq = 8 -> at most 32 splits
+    assert fa.decode_paged_workspace_bytes(1, 8, 8, 4096, 256, 128) == rows * 4 + rows * 128 * 4 + 4
+    rows = 2 * 8 * 8                         # max_seq 4096 -> 8 splits
+    assert fa.decode_paged_workspace_bytes(2, 8, 2, 64, 64, 64) == 33288 == 512 + rows * 64 * 4 + 8
+    assert fa.decode_paged_workspace_bytes(3, 8, 2, 1, 32, 64) == 0      # 32 keys: one split
+    assert fa.decode_paged_workspace_bytes(2, 8, 2, 4, 48, 64) == 0      # bad page size
+    assert fa.decode_paged_workspace_bytes(2, 8, 2, 4, 64, 96) == 0      # bad head dim
+    assert fa.decode_paged_workspace_bytes(2, 8, 3, 4, 64, 64) == 0      # H % Hkv != 0
 
 
 def _quant(**kw):

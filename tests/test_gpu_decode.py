@@ -223,3 +223,61 @@ def test_paged_ragged_poisoned_workspace_many_splits():
         o_ref, l_ref = oracle.attention(widen(q[b:b + 1], "bf16"), widen(k[b:b + 1, :, :L], "bf16"),
                                         widen(v[b:b + 1, :, :L], "bf16"), False, 0.125)
         compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, "bf16", f"paged poisoned b={b}")
+
+
+def test_paged_auto_full_length_equals_forced_splits():
+    """Automatic splits at full length: 4 sequences of 2,048 keys, 2 KV
+    heads -> a chunk of 512 keys, i.e. the partition of 4 forced splits, so
+    the bits are the same (only the workgroup order differs)."""
+    need_gpu()
+    B, H, Hkv, d, ps, L = 4, 8, 2, 64, 64, 2048
+    announce("fa_decode_paged automatic vs 4 forced splits, full length")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, [L] * B, ps, d, "bf16", seed=11)
+    args = (to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"), torch.from_numpy(table).cuda(),
+            torch.full((B,), L, dtype=torch.int32, device="cuda"))
+    o1, l1 = fa.decode_paged(*args, scale=0.125, num_splits=4)
+    o2, l2 = fa.decode_paged(*args, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_auto_skewed_lengths_poisoned_workspace(d):
+    """Automatic splits on a skewed batch of 70 sequences (more than one
+    64-lane block of the device-side scan): one long sequence, the rest
+    empty or a few keys; the workspace starts as NaN."""
+    need_gpu()
+    B, H, Hkv, ps, dt = 70, 4, 2, 32, "f16" if d == 128 else "bf16"
+    rng = np.random.default_rng(d)
+    lens = [int(x) for x in rng.choice([0, 1, 5, 31, 40], B)]
+    lens[37] = 3000
+    announce(f"fa_decode_paged automatic, skewed lengths, B={B} d={d}")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, lens, ps, d, dt, seed=d + 3)
+    ws = fa.decode_paged_workspace(B, H, Hkv, max_pages, ps, d)
+    ws.fill_(255)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=scale,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b])), b
+            continue
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, scale)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, dt, f"paged auto b={b} L={L}")
+
+
+def test_paged_auto_all_empty():
+    need_gpu()
+    B, H, Hkv, d, ps = 5, 8, 2, 64, 128
+    announce("fa_decode_paged automatic, every sequence empty")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, [0] * B, ps, d, "bf16", seed=2,
+                                                        extra_pages=2)
+    o, lse = fa.decode_paged(to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                             torch.from_numpy(table).cuda(),
+                             torch.zeros(B, dtype=torch.int32, device="cuda"), scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))

@@ -126,7 +126,7 @@ def test_random_paged_decode(seed):
              f"page={ps} lens={lens} splits={splits}")
     q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, lens, ps, d, dt, seed=seed)
     scale = float(np.float32(1 / math.sqrt(d)))
-    ws = fa.decode_workspace(B, H, Hkv, max_pages * ps, d, splits)
+    ws = fa.decode_paged_workspace(B, H, Hkv, max_pages, ps, d, splits)
     if ws is not None:
         ws.fill_(255)
     o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
