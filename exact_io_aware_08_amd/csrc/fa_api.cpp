@@ -250,7 +250,7 @@ fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_page
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
     const int hq = Hkv * ((H / Hkv + 15) / 16);  // workgroups per (sequence, split)
-    const bool auto_split = num_splits == 0;
+    const bool auto_split = num_splits == 0 && B <= fa::kPagedAutoMaxBatch;
     const int splits = auto_split ? fa::paged_auto_max_splits(max_seq, hq)
                                   : fa_decode_splits(B, H, Hkv, (int)max_seq, num_splits);
     const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits, auto_split);
@@ -286,7 +286,8 @@ size_t fa_decode_paged_workspace_bytes(int B, int H, int Hkv, int max_pages, int
         return 0;
     const long long max_seq = (long long)max_pages * page_size;
     if (max_seq > kMaxSlice / 128) return 0;
-    if (num_splits > 0) return fa_decode_workspace_bytes(B, H, Hkv, (int)max_seq, d, num_splits);
+    if (num_splits > 0 || B > fa::kPagedAutoMaxBatch)
+        return fa_decode_workspace_bytes(B, H, Hkv, (int)max_seq, d, num_splits);
     const int hq = Hkv * ((H / Hkv + 15) / 16);
     return decode_layout(B, H, Hkv, d, fa::paged_auto_max_splits(max_seq, hq), true).total;
 }

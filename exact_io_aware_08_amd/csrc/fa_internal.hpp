@@ -96,6 +96,11 @@ constexpr int kDecodeStep = 128;   // keys per decode workgroup step (4 waves x 
 // the pairs never number more than ceil(kPagedTargetItems / hq) + B.
 constexpr int kPagedTargetItems = 256;
 constexpr int kPagedMinChunk = 512;
+// Every workgroup scans the lengths 64 at a time (one dependent load per 64
+// sequences), so automatic splits serve batches of up to this many
+// sequences; larger batches take the uniform split, which already yields
+// enough workgroups.
+constexpr int kPagedAutoMaxBatch = 256;
 inline int paged_auto_max_splits(long long max_seq, int hq)
 {
     const long long by_len = (max_seq + kPagedMinChunk - 1) / kPagedMinChunk;

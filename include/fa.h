@@ -186,12 +186,13 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
  *     ceil(max_pages * page_size / num_splits) keys (rounded up to the split
  *     granularity), as fa_decode with Nk = max_pages * page_size; the chunks
  *     past a sequence's end do no work.
- *   num_splits = 0 (automatic): the kernels read the lengths on the device
- *     and size one chunk for the whole batch, about 256 workgroups' worth of
- *     keys in all (at least 512 keys, a multiple of the split granularity);
- *     sequence b gets max(1, ceil(seq_lens[b] / chunk)) splits.  A ragged
- *     batch is then spread over the whole GPU instead of following its
- *     longest sequence.  No host synchronisation.
+ *   num_splits = 0 (automatic), B <= 256: the kernels read the lengths on
+ *     the device and size one chunk for the whole batch, about 256
+ *     workgroups' worth of keys in all (at least 512 keys, a multiple of the
+ *     split granularity); sequence b gets max(1, ceil(seq_lens[b] / chunk))
+ *     splits.  A ragged batch is then spread over the whole GPU instead of
+ *     following its longest sequence.  No host synchronisation.  B > 256:
+ *     the split count fa_decode would choose for Nk = max_pages * page_size.
  *   workspace: device memory of at least fa_decode_paged_workspace_bytes(B,
  *     H, Hkv, max_pages, page_size, d, num_splits) bytes (none when that is
  *     0), 16-byte aligned; contents on entry do not matter.

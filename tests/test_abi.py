@@ -228,6 +228,11 @@ def test_paged_workspace_sizes():
     rows = 2 * 8 * 8                         # max_seq 4096 -> 8 splits
     assert fa.decode_paged_workspace_bytes(2, 8, 2, 64, 64, 64) == 33288 == 512 + rows * 64 * 4 + 8
     assert fa.decode_paged_workspace_bytes(3, 8, 2, 1, 32, 64) == 0      # 32 keys: one split
+    # more than 256 sequences: the uniform split (no per-sequence counts)
+    assert fa.decode_paged_workspace_bytes(257, 8, 2, 64, 128, 64) == \
+        fa.decode_workspace_bytes(257, 8, 2, 8192, 64)
+    assert fa.decode_paged_workspace_bytes(256, 8, 2, 64, 128, 64) != \
+        fa.decode_workspace_bytes(256, 8, 2, 8192, 64)
     assert fa.decode_paged_workspace_bytes(2, 8, 2, 4, 48, 64) == 0      # bad page size
     assert fa.decode_paged_workspace_bytes(2, 8, 2, 4, 64, 96) == 0      # bad head dim
     assert fa.decode_paged_workspace_bytes(2, 8, 3, 4, 64, 64) == 0      # H % Hkv != 0

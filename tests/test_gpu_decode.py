@@ -281,3 +281,25 @@ def test_paged_auto_all_empty():
                              torch.zeros(B, dtype=torch.int32, device="cuda"), scale=0.125)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_paged_large_batch_uses_uniform_split():
+    """Past 256 sequences the automatic mode takes the uniform split; 260
+    short ragged sequences (some empty) against the oracle."""
+    need_gpu()
+    B, H, Hkv, d, ps = 260, 4, 1, 64, 32
+    rng = np.random.default_rng(260)
+    lens = [int(x) for x in rng.integers(0, 90, B)]
+    announce(f"fa_decode_paged B={B}, automatic mode past 256 sequences")
+    q, k, v, kp, vp, table, max_pages, _ = _paged_case(B, H, Hkv, lens, ps, d, "bf16", seed=260)
+    o, lse = fa.decode_paged(to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=0.125)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b])), b
+            continue
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], "bf16"), widen(k[b:b + 1, :, :L], "bf16"),
+                                        widen(v[b:b + 1, :, :L], "bf16"), False, 0.125)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, "bf16", f"paged B=260 b={b} L={L}")
