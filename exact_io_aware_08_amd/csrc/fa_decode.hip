@@ -42,7 +42,12 @@
 // block table maps each sequence's logical pages to physical pages, the
 // KV-cache management of serving systems the "FlashAttention (IT)" entry
 // mentions under "Soluzioni specializzate"); only the address of each
-// wave's 32-key block changes.
+// wave's 32-key block changes.  A paged batch can also be split from its
+// lengths, which only the device knows: every workgroup reads them, takes
+// one chunk size for the whole batch (about kPagedTargetItems workgroups in
+// all) and finds its (sequence, split) pair with a prefix sum over the
+// lanes, so a ragged or skewed batch fills the GPU instead of following its
+// longest sequence.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
