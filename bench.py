@@ -287,7 +287,11 @@ def main():
         pws = fa.decode_paged_workspace(B4, H4, Hkv4, npg, ps, d4, device=dev)
         lens_full = torch.full((B4,), Nk4, dtype=torch.int32, device=dev)
         lens_rag = torch.randint(1, Nk4 + 1, (B4,), generator=gen, dtype=torch.int32)
-        for name, lens in (("full", lens_full), ("ragged", lens_rag.to(dev))):
+        # skewed: one sequence at full length, the others at 100 keys
+        lens_skew = torch.full((B4,), 100, dtype=torch.int32)
+        lens_skew[3] = Nk4
+        ws4 = fa.decode_paged_workspace(B4, H4, Hkv4, npg, ps, d4, 4, device=dev)
+        for name, lens in (("full", lens_full), ("ragged", lens_rag.to(dev)), ("skewed", lens_skew.to(dev))):
             pus = 1e3 * _timed(lambda i: fa.decode_paged(q4, pcaches[i % 4][0], pcaches[i % 4][1],
                                                          table, lens, scale=c4["scale"],
                                                          workspace=pws, out=o4, lse=l4),
@@ -296,6 +300,12 @@ def main():
             pbytes = 2 * Hkv4 * kv_keys * d4 * 2 + B4 * H4 * d4 * 2 * 2 + B4 * H4 * 4
             paged[name] = {"us_per_call": round(pus, 2), "keys": kv_keys,
                            "GB/s": round(pbytes / (pus * 1e-6) / 1e9, 1)}
+            if name != "full":  # the uniform split sized for the table's capacity, for comparison
+                f4 = 1e3 * _timed(lambda i: fa.decode_paged(q4, pcaches[i % 4][0], pcaches[i % 4][1],
+                                                            table, lens, scale=c4["scale"], num_splits=4,
+                                                            workspace=ws4, out=o4, lse=l4),
+                                  args.decode_steps, 400, torch)
+                paged[name]["us_per_call_4_uniform_splits"] = round(f4, 2)
         dec["paged"] = paged
         out.setdefault("timing", {})["decode_per_call"] = _dist(
             lambda i: fa.decode(q4, caches[i % 4][0], caches[i % 4][1], scale=c4["scale"],
