@@ -145,13 +145,15 @@ def _sweep(torch, fa, fagen, to_dev, dev):
                              "extra_bytes": int(mem_b)}
         else:
             row["fa_bwd"] = None  # the backward kernels take d = 64 and 128
-        kt = k.transpose(-1, -2).contiguous()
-        mask = torch.ones(N, N, dtype=torch.bool, device=dev).triu(1)
+        kt = k[0].transpose(-1, -2).contiguous()   # [H, d, N]
+        # additive causal bias: 0 on and below the diagonal, -inf above it
+        bias = torch.full((N, N), float("-inf"), dtype=torch.bfloat16, device=dev).triu(1)
 
         def materialised():
-            sc = torch.matmul(q, kt) * scale
-            sc.masked_fill_(mask, float("-inf"))
-            return torch.matmul(torch.softmax(sc, dim=-1), v)
+            # the whole H x N x N score matrix in device memory, in three
+            # separate tensor ops: biased logits, row softmax, weighted V rows
+            logits = torch.baddbmm(bias, q[0], kt, alpha=scale)
+            return torch.bmm(torch.softmax(logits, dim=-1), v[0]).unsqueeze(0)
 
         om, mem_m = peak(materialised)
         ms_m = _timed(lambda i: materialised(), max(3, it // 4), 2, torch, qa)
@@ -241,8 +243,17 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic},
         })
-        out.setdefault("timing", {})["prefill_per_call"] = _dist(
-            lambda i: fa.fwd(q3, k3, v3, causal=True, scale=c3["scale"], out=o3, lse=l3), 50, torch)
+        pc = _dist(lambda i: fa.fwd(q3, k3, v3, causal=True, scale=c3["scale"], out=o3, lse=l3),
+                   50, torch)
+        out.setdefault("timing", {})["prefill_per_call"] = pc
+        # `frac` is from the mean of the K timed calls; the median of 50 single
+        # calls timed right after them (the clock has settled by then) is the
+        # steady-state figure, the one a kernel-trace average reproduces
+        steady = flops / (pc["median_ms"] * 1e-3) / 1e12
+        out["roofline"].update({
+            "frac_basis": "mean of the K timed calls (HIP events on the launch stream)",
+            "achieved_steady": round(steady, 2), "frac_steady": round(steady / PEAK_BF16_TFLOPS, 4),
+            "steady_basis": "median of 50 single calls after the timed region"})
 
     # ---------------- decode ----------------
     if args.only in ("all", "decode"):
@@ -484,29 +495,58 @@ def main():
                                   "gflops_fp64": round(4.0 * cf["d"] * npairs / dt / 1e9, 3)}
         out["cpu_baseline"]["other_configs"] = others
     if "other_workloads" in out and not args.no_cpu_baseline:
-        # the P-cast report against the oracle: closed-form flush fraction
-        # F(Delta, S) and MSE against exact attention on sampled rows
+        # The P-cast report against the oracle, per Delta and run:
+        #  * MSE against exact attention on 32 seeded rows per head, with the
+        #    stated MSE bound (mean squared per-element bound) on the same rows;
+        #  * the closed-form flush fraction F(Delta, S);
+        #  * the oracle's emulation counts over every row of heads 0-3, beside
+        #    the GPU counters of a run on the same four heads (the GPU counters
+        #    over all 32 heads are in "casts"/"flushed").
         import oracle
         d4 = oracle.expected_max_gauss(4)
         c5 = fagen.WORKLOADS["pcast_sink_f32"]
         B5, H5, N5, d5 = c5["B"], c5["H"], c5["Nq"], c5["d"]
-        rows5 = np.stack([fagen.sample_rows(1, h, N5, 8) for h in range(H5)])
+        rows5 = np.stack([fagen.sample_rows(1, h, N5, 32) for h in range(H5)])
         q5n, k5n, v5n = fagen.sink_inputs(0, B5, H5, N5, d5, 0.0)
+        nthr = oracle.default_threads()
+        HS = 4  # heads of the emulated slice
+        tile5 = fa.kv_tile(torch.float32, d5, pcast=True)
         for delta in c5["deltas"]:
             k5n_d = k5n.copy()
             k5n_d[:, :, :4, 0] += np.float32(delta * math.sqrt(d5))
-            o_ex, _ = oracle.attention(q5n, k5n_d, v5n, True, c5["scale"], rows=rows5,
-                                       nthreads=oracle.default_threads())
+            o_ex, _ = oracle.attention(q5n, k5n_d, v5n, True, c5["scale"], rows=rows5, nthreads=nthr)
+            probs = [np.stack([oracle.attention_probs(q5n, k5n_d, True, c5["scale"], 0, h, int(i))
+                               for i in rows5[h]]) for h in range(H5)]
             k5d = to_dev(k5n_d, "f32")
             q5d, v5d = to_dev(q5n, "f32"), to_dev(v5n, "f32")
+            qs, ks, vs = (x[:, :HS].contiguous() for x in (q5d, k5d, v5d))
             for name, (S, rev) in (("fwd_S1", (1.0, False)), ("rev_S256", (256.0, True))):
                 o5, _, _ = fa.fwd_pcast(q5d, k5d, v5d, causal=True, scale=c5["scale"], p_scale=S,
                                         kv_reverse=rev, n_sink=4)
                 og = o5.cpu().numpy()[0][np.arange(H5)[:, None], rows5]
                 r = out["other_workloads"]["pcast_sink_f32"]["runs"][f"delta{delta:g}_{name}"]
                 r["mse_vs_exact_sampled"] = float(np.mean((og - o_ex[0]) ** 2))
+                bsq = sum(float(np.sum(oracle.pcast_bound(probs[h], v5n[0, h], S) ** 2))
+                          for h in range(H5))
+                r["mse_stated_bound"] = bsq / og.size
                 r["F_closed_form"] = float(oracle.F_closed_form(delta, S, d4))
-        out["other_workloads"]["pcast_sink_f32"]["mse_rows"] = "8 seeded rows per head"
+                _, _, cs = fa.fwd_pcast(qs, ks, vs, causal=True, scale=c5["scale"], p_scale=S,
+                                        kv_reverse=rev, n_sink=4)
+                cs = [int(x) for x in cs.cpu()]
+                _, _, ce = oracle.pcast_emulate(q5n[:, :HS], k5n_d[:, :HS], v5n[:, :HS], True,
+                                                c5["scale"], tile5, S, rev, 4, nthreads=nthr)
+                r["heads_0_3"] = {
+                    "gpu": {"casts": cs[0], "flushed": cs[1], "flushed_outside_sink_tiles": cs[3]},
+                    "emulation": {"casts": ce[0], "flushed": ce[1], "flushed_outside_sink_tiles": ce[3],
+                                  "flush_frac": ce[1] / max(ce[0], 1)},
+                    "max_rel_count_diff": max(abs(a - b) / max(b, 1) for a, b in zip(cs, ce))}
+            del k5d, q5d, v5d, qs, ks, vs
+        out["other_workloads"]["pcast_sink_f32"]["mse_rows"] = (
+            "32 seeded rows per head; mse_stated_bound = mean over those rows of the squared "
+            "per-element bound of the P-cast analysis (oracle.pcast_bound)")
+        out["other_workloads"]["pcast_sink_f32"]["emulation_sample"] = (
+            "oracle emulation over every row of heads 0-3 (1/8 of the workload), beside the GPU "
+            "counters of a run on the same four heads")
         # the page's own setting: N = 4096, MSE of each cast setting against exact attention
         N6 = 4096
         rows6 = np.stack([fagen.sample_rows(2, h, N6, 8) for h in range(H5)])

@@ -1,8 +1,10 @@
 """libfa -- exact IO-aware attention for AMD MI355X (gfx950).
 
 Thin Python binding over the C ABI of include/fa.h: it checks tensor
-placement, dtype and layout, allocates outputs with torch and passes raw
-device pointers plus torch's current HIP stream.  Every step of the
+placement, dtype, shape and layout -- of the inputs and of every output or
+workspace the caller passes in, because the C ABI receives raw pointers and
+cannot size-check them -- allocates outputs with torch and passes raw device
+pointers plus torch's current HIP stream.  Every step of the
 computation runs in the HIP kernels of libfa.so; there is no Python or CPU
 path.
 
@@ -42,6 +44,35 @@ def _check_tensor(name, t, ndim):
         raise ValueError(f"{name}: unsupported dtype {t.dtype}")
 
 
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output: exact shape and dtype, on `device`,
+    contiguous.  Raises before anything is launched (an undersized or
+    mistyped buffer would otherwise be written out of bounds)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(t, device):
+    """A caller-supplied workspace: any dtype, on `device`, contiguous (its
+    byte size is checked by the C ABI against what the call needs)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _qkv_shapes(q, k, v):
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(n, t, 4)
@@ -62,6 +93,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _check_out("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, Nq), torch.float32, q.device)
     o = out if out is not None else torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -82,6 +117,12 @@ def fwd_pcast(q, k, v, causal: bool = True, scale: float | None = None, p_scale:
     B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v)
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is not None:
+        _check_out("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, Nq), torch.float32, q.device)
+    if counts is not None:  # the kernel adds four uint64 values into it
+        _check_out("counts", counts, (4,), torch.int64, q.device)
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -133,8 +174,14 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
         raise ValueError("decode takes one query token per (batch, head)")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _check_out("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, 1), torch.float32, q.device)
     if workspace is None:
         workspace = decode_workspace(B, H, Hkv, Nk, d, num_splits, q.device)
+    else:
+        _check_workspace(workspace, q.device)
     o = out if out is not None else torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
@@ -164,12 +211,17 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
         raise ValueError("lse must be a contiguous fp32 [B, H, Nq] tensor on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_out(name, t, ref.shape, ref.dtype, q.device)
     dq = dq if dq is not None else torch.empty_like(q)
     dk = dk if dk is not None else torch.empty_like(k)
     dv = dv if dv is not None else torch.empty_like(v)
     if workspace is None:
         n = bwd_workspace_bytes(B, H, Nq)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, q.device)
     st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Nq,
                        Nk, d, int(bool(causal)), float(scale), _DT[q.dtype], workspace.data_ptr(),
@@ -199,8 +251,14 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float | None
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _check_out("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, 1), torch.float32, q.device)
     if workspace is None:
         workspace = decode_paged_workspace(B, H, Hkv, max_pages, page_size, d, num_splits, q.device)
+    else:
+        _check_workspace(workspace, q.device)
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
@@ -237,11 +295,15 @@ def quant_e4m3(x, signs=None, layout: str = "rows32", whole: bool = False, codes
     _check_tensor("x", x, 4)
     B, H, N, d = x.shape
     lay = {"rows32": 0, "channels": 1}[layout]
+    sshape = (B, H, (N + 31) // 32 if lay == 0 else d)
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    else:
+        _check_out("codes", codes, x.shape, torch.uint8, x.device)
     if scales is None:
-        scales = torch.empty((B, H, (N + 31) // 32 if lay == 0 else d), dtype=torch.float32,
-                             device=x.device)
+        scales = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    else:
+        _check_out("scales", scales, sshape, torch.float32, x.device)
     if signs is not None and (signs.device != x.device or signs.dtype != torch.float32
                               or signs.numel() != d or not signs.is_contiguous()):
         raise ValueError("signs must be a contiguous fp32 tensor of d values on x's device")
@@ -279,6 +341,10 @@ def fwd_fp8(q, k, v, q_scales, k_scales, v_scales, causal: bool = False,
             raise ValueError(f"{n} must be a contiguous fp32 tensor of shape {shp} on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _check_out("out", out, (B, H, Nq, d), out_dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, Nq), torch.float32, q.device)
     o = out if out is not None else torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)

@@ -304,3 +304,51 @@ def expected_max_gauss(k: int) -> float:
 
 def dp(S: float) -> float:
     return _load().orc_dp(float(S))
+
+
+def pcast_bound(a_rows, v_rows, S: float, slack: float = 2e-5) -> np.ndarray:
+    """The stated per-element error bound of the E4M3 P-cast (the analysis of
+    gist.science "Resumen Tecnico: Precision de P-Cast en la Atencion FP8",
+    sections "Marco Teorico" and "Optimizacion 2"), around exact attention.
+
+    a_rows: [R, Nk] exact weights (rows of the softmax); v_rows: [Nk, d] (or
+    [R, Nk, d]).  Returns the bound [R, d] on |O_pcast - O_exact|.
+
+    With p_j = a_j / max(a) the probability relative to the row's final
+    maximum, casting S*p to E4M3 with round-to-nearest-even moves each weight
+    by a relative amount r_j:
+      r_j = 2^-4                    if S*p_j >= 2^-6 (normal: half an ulp of a
+                                    3-bit mantissa),
+      r_j = min(1, 2^-10 / (S*p_j)) otherwise (subnormal grid 2^-9, half step
+                                    2^-10; a flushed value loses all of it).
+    A running maximum never exceeds the final one, so the p a kernel casts is
+    at least p_j and the same r_j bounds its error.  The normaliser is the sum
+    of the uncast p, so |O_pcast - O| <= sum_j a_j r_j |v_j| per element;
+    `slack` covers fp32 rounding of logits, exponentials and sums.  The stated
+    MSE bound is the mean of the squared per-element bounds.
+    """
+    a_rows = np.asarray(a_rows, dtype=np.float64)
+    mx = a_rows.max(axis=1, keepdims=True)
+    p = np.divide(a_rows, mx, out=np.zeros_like(a_rows), where=mx > 0)
+    sp = S * p
+    with np.errstate(divide="ignore"):
+        r = np.where(sp >= 2.0 ** -6, 2.0 ** -4, np.minimum(1.0, 2.0 ** -10 / sp))
+    r = np.where(a_rows > 0, r, 0.0)
+    av = np.abs(np.asarray(v_rows, dtype=np.float64))
+    if av.ndim == 2:
+        core = (a_rows * r) @ av
+        scl = a_rows @ av
+    else:
+        core = np.einsum("rj,rjc->rc", a_rows * r, av)
+        scl = np.einsum("rj,rjc->rc", a_rows, av)
+    return core + slack * scl + 1e-7
+
+
+def pcast_bound_rows(q, k, v, causal: bool, scale: float, S: float, b: int, h: int,
+                     rows) -> np.ndarray:
+    """pcast_bound for the given query rows of (b, h): the exact weights come
+    from orc_attention_probs, the value rows from v's KV head.  [R, d]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    H, Hkv = q.shape[1], k.shape[1]
+    a = np.stack([attention_probs(q, k, causal, scale, b, h, int(i)) for i in rows])
+    return pcast_bound(a, v[b, h // (H // Hkv)], S)

@@ -278,39 +278,48 @@ def pin_split_merge():
 
 
 def _online(q, k, v, causal, scale, Bc, deferred):
-    """Tile-by-tile online softmax for one (b,h) slice in fp64."""
+    """Tile-by-tile softmax for one (b,h) slice in fp64, in two forms that the
+    recurrence of [MM] "La recurrencia de softmax en linea" makes equal to the
+    two-pass definition:
+      deferred=True:  running max m, unnormalised sum l and accumulator, one
+                      division at the end (the form of "FA2: paralelismo");
+      deferred=False: every tile is reduced to its own normalised state
+                      (O_t, lse_t) -- a softmax-weighted mean of its V rows
+                      and the log-sum-exp of its logits -- and folded into the
+                      running normalised state with the log-sum-exp identity
+                      lse' = log(e^lse + e^lse_t),
+                      O' = e^(lse - lse') O + e^(lse_t - lse') O_t,
+                      the same associativity the split-KV merge relies on."""
     Nq, d = q.shape
     Nk = k.shape[0]
     O = np.zeros((Nq, d))
     LSE = np.zeros(Nq)
     for i in range(Nq):
         lim = _visible(i, Nq, Nk, causal)
-        m, l, acc = -math.inf, 0.0, np.zeros(d)
+        m, l, acc = -math.inf, 0.0, np.zeros(d)     # deferred state
+        lse, o = -math.inf, np.zeros(d)              # normalised state
         for j0 in range(0, lim, Bc):
             j1 = min(lim, j0 + Bc)
             s = scale * (k[j0:j1].astype(np.float64) @ q[i].astype(np.float64))
             vj = v[j0:j1].astype(np.float64)
-            if deferred:   # running max, unnormalised accumulator, one division at the end
+            if deferred:
                 mn = max(m, s.max())
                 a = math.exp(m - mn) if m > -math.inf else 0.0
                 p = np.exp(s - mn)
                 l = a * l + p.sum()
                 acc = a * acc + p @ vj
                 m = mn
-            else:          # tile-local max, normalised after every tile
-                mt = s.max()
-                p = np.exp(s - mt)
-                lt = p.sum()
-                mn = max(m, mt)
-                a = math.exp(m - mn) if m > -math.inf else 0.0
-                ln = l * a + lt * math.exp(mt - mn)
-                acc = acc * (l * a / ln) + (p @ vj) * (math.exp(mt - mn) / ln)
-                m, l = mn, ln
+            else:
+                lse_t = float(np.logaddexp.reduce(s))
+                o_t = np.exp(s - lse_t) @ vj
+                lse_n = float(np.logaddexp(lse, lse_t))
+                o = math.exp(lse - lse_n) * o + math.exp(lse_t - lse_n) * o_t
+                lse = lse_n
         if lim == 0:
             LSE[i] = -math.inf
             continue
-        O[i] = acc / l if deferred else acc
-        LSE[i] = m + math.log(l)
+        O[i] = acc / l if deferred else o
+        LSE[i] = m + math.log(l) if deferred else lse
     return O, LSE
 
 
@@ -635,9 +644,9 @@ def pin_pcast_single_key():
 
 
 def pin_pcast_error_bound():
-    """The emulation stays within the per-element bound of tests/pcast_bounds.py
+    """The emulation stays within the per-element bound of oracle.pcast_bound
     around exact attention, for both orders and several S."""
-    from pcast_bounds import pcast_bound
+    pcast_bound = oracle.pcast_bound
     q, k, v = _inputs(1, 2, 2, 150, 150, 16, seed=63, sc=1.7)
     q[..., 0] = 1.0
     k[:, :, :4, 0] += 9.0 * 4.0   # strong sink: many flushes at S = 1 forward

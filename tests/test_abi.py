@@ -160,6 +160,35 @@ def test_binding_rejects_cpu_tensors():
         fa.fwd(x, x, x)
 
 
+def test_binding_output_checks():
+    """Caller-supplied outputs are checked for exact shape, dtype, device and
+    contiguity before any launch (the C ABI cannot size-check raw pointers):
+    the helper every entry point uses, exercised on CPU tensors."""
+    import torch
+    dev = torch.device("cpu")
+    good = torch.zeros(2, 3, 5, 64, dtype=torch.bfloat16)
+    fa._check_out("out", good, (2, 3, 5, 64), torch.bfloat16, dev)
+    bad = [
+        (torch.zeros(2, 3, 4, 64, dtype=torch.bfloat16), (2, 3, 5, 64), torch.bfloat16),  # short
+        (torch.zeros(2, 3, 5, 64, dtype=torch.float16), (2, 3, 5, 64), torch.bfloat16),   # dtype
+        (torch.zeros(2, 3, 64, 5, dtype=torch.bfloat16).transpose(-1, -2), (2, 3, 5, 64),
+         torch.bfloat16),                                                                   # strided
+        (torch.zeros(4, dtype=torch.int32), (4,), torch.int64),                             # counts
+        (torch.zeros(3, dtype=torch.int64), (4,), torch.int64),
+        (torch.zeros(2, 3, 5), (2, 3, 6), torch.float32),                                   # lse
+    ]
+    for t, shape, dt in bad:
+        with pytest.raises(ValueError):
+            fa._check_out("x", t, shape, dt, dev)
+    with pytest.raises(ValueError):
+        fa._check_out("x", good, (2, 3, 5, 64), torch.bfloat16, torch.device("meta"))
+    with pytest.raises(TypeError):
+        fa._check_out("x", None, (1,), torch.float32, dev)
+    fa._check_workspace(torch.zeros(100, dtype=torch.uint8), dev)
+    with pytest.raises(ValueError):
+        fa._check_workspace(torch.zeros(10, 10, dtype=torch.uint8).t(), dev)
+
+
 def _bwd(ws_bytes=None, **kw):
     a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=2, Nq=64, Nk=64,
              d=64, causal=1, scale=0.125, dtype=BF16, ws=P)

@@ -27,7 +27,7 @@ import exact_io_aware_08_amd as fa
 import fagen
 import oracle
 from gpu_util import announce, need_gpu, to_dev, widen
-from pcast_bounds import pcast_bound
+from oracle import pcast_bound
 
 pytestmark = pytest.mark.gpu
 

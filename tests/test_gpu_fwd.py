@@ -1,8 +1,10 @@
 """GPU parity of fa_fwd (prefill) against the fp64 oracle, through the C ABI.
 
-Full-size workloads are checked on seeded sampled rows (the oracle computes
-them one by one); smaller shapes that still span several tiles and ragged
-tails are checked on every output.  Tolerances: tests/gpu_util.py.
+Every output row is compared for the GPT-2-small-shaped workload, for the
+256-row-workgroup kernel the trading day runs (bf16 and fp16), and for the
+smaller shapes that span several tiles and ragged tails; the trading day
+itself is compared on seeded sampled rows (its whole-row comparison is the
+bench's parity leg).  Tolerances: tests/gpu_util.py.
 """
 import math
 
@@ -56,11 +58,12 @@ def _sampled_rows(B, H, N, n, seed=0):
     return np.stack([r[:width] for r in rows])
 
 
-def test_gpt2_small_prefill_bf16_sampled():
-    """B=4, H=12, N=2048, d=64, bf16, causal: 128 sampled rows per head plus
-    the first and last row."""
-    rows = _sampled_rows(4, 12, 2048, 128)
-    run_case(4, 12, 12, 2048, 2048, 64, "bf16", True, rows=rows)
+def test_gpt2_small_prefill_bf16_all_rows():
+    """B=4, H=12, N=2048, d=64, bf16, causal, seed 0: every row of every head
+    (98,304 rows) against the oracle."""
+    c = fagen.WORKLOADS["gpt2s_prefill_bf16"]
+    m = run_case(c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"], "bf16", True, scale=c["scale"])
+    announce(f"  gpt2-small all rows: {m}")
 
 
 def test_trading_day_prefill_bf16_sampled():
@@ -165,13 +168,42 @@ def test_lse_optional_and_stream():
     compare(o, None, o_ref, None, "bf16", "side stream")
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_large_grid_uses_256_row_tiles(causal):
-    """ceil(N/256)*B*H >= 1024 selects the 256-row workgroups (32-key tiles);
-    smaller grids use 128-row workgroups.  Ragged N, GQA, sampled rows that
-    include the last row of every head."""
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("bf16", False), ("f16", True),
+                                       ("f16", False)])
+def test_large_grid_uses_256_row_tiles(dt, causal):
+    """ceil(N/256)*B*H >= 1024 selects the 256-row workgroups (two 32-row
+    query blocks per wave, 32-key tiles) -- the kernel instance the trading
+    day runs; smaller grids use 128-row workgroups.  B=8, H=16, Hkv=4,
+    N=2000 gives exactly 1,024 such workgroups with a ragged last query tile
+    (2000 = 7*256 + 208) and a ragged last key tile; every row of every head
+    is compared."""
     B, H, Hkv, N = 8, 16, 4, 2000
+    assert -(-N // 256) * B * H == 1024
     assert fa.kv_tile(torch.bfloat16, 64) == 32
-    rows = _sampled_rows(B, H, N, 24)
-    m = run_case(B, H, Hkv, N, N, 64, "bf16", causal, seed=21, rows=rows)
-    assert m["max_abs"] <= 2e-2
+    m = run_case(B, H, Hkv, N, N, 64, dt, causal, seed=21 + int(causal) + 2 * (dt == "f16"))
+    announce(f"  256-row workgroups {dt} causal={causal}: {m}")
+
+
+def test_caller_outputs_are_checked():
+    """Outputs passed in by the caller must match exactly (shape, dtype,
+    device, contiguity); a mismatch raises before any launch and leaves the
+    buffer untouched."""
+    need_gpu()
+    announce("fa_fwd / fa_fwd_pcast / fa_decode output checks")
+    q = torch.randn(1, 2, 70, 64, device="cuda").to(torch.bfloat16)
+    for kw in (dict(out=torch.empty(1, 2, 69, 64, device="cuda", dtype=torch.bfloat16)),
+               dict(out=torch.empty(1, 2, 70, 64, device="cuda", dtype=torch.float16)),
+               dict(lse=torch.empty(1, 2, 69, device="cuda")),
+               dict(lse=torch.empty(1, 2, 70, device="cuda", dtype=torch.float16))):
+        with pytest.raises(ValueError):
+            fa.fwd(q, q, q, causal=True, **kw)
+    x = torch.randn(1, 2, 70, 64, device="cuda")
+    cnt = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd_pcast(x, x, x, counts=cnt)
+    torch.cuda.synchronize()
+    assert torch.all(cnt == 7)
+    qd = torch.randn(2, 8, 1, 64, device="cuda").to(torch.bfloat16)
+    kv = torch.randn(2, 2, 300, 64, device="cuda").to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.decode(qd, kv, kv, out=torch.empty(2, 8, 64, device="cuda", dtype=torch.bfloat16))

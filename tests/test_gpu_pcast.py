@@ -6,9 +6,12 @@
   GPU's fp32 exp and the oracle's differ by an ulp), MSE within 5%, and every
   output element within the stated error bound around exact attention.
 * On the full sink workload (B=1, H=32, N=8192, d=128) for Delta in
-  {4, 6, 8, 10}: forward/S=1 and reverse/S=256 runs, the bound on sampled
-  rows, the flush fraction against the closed form F(Delta,S) of the P-cast
-  page, and zero flushes before the sink block under reverse order.
+  {4, 6, 8, 10}: forward/S=1 and reverse/S=256 runs, all four counters
+  against the emulation over every row (within 0.01%), every element against
+  the emulation, MSE against exact attention on 256 rows per head within 5%
+  of the emulation's and below the stated MSE bound, the flush fraction
+  against the closed form F(Delta,S) of the P-cast page, and zero flushes
+  before the sink block under reverse order.
 """
 import math
 
@@ -20,7 +23,7 @@ import exact_io_aware_08_amd as fa
 import fagen
 import oracle
 from gpu_util import announce, need_gpu, to_dev
-from pcast_bounds import pcast_bound
+from oracle import pcast_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -89,15 +92,39 @@ def _model_flush(delta, S, n=400_000):
     return float(np.mean(S * np.exp(z - M) <= 2.0 ** -10))
 
 
+def _counts_match(cnt, ce):
+    """GPU counters against the emulation's: each within 0.01% of the
+    emulation's count, plus 2 for casts that flip at the round-to-zero
+    threshold where the GPU's fp32 exponential and the emulation's differ by
+    an ulp."""
+    return all(abs(cnt[i] - ce[i]) <= 1e-4 * ce[i] + 2 for i in range(4))
+
+
 @pytest.mark.parametrize("delta", [4.0, 6.0, 8.0, 10.0])
 def test_pcast_sink_workload_full_size(delta):
-    """B=1, H=32, N=8192, d=128, causal, sink keys 0..3 shifted by Delta."""
+    """B=1, H=32, N=8192, d=128, causal, sink keys 0..3 shifted by Delta;
+    forward order with S=1 and reverse order with S=256.
+
+    * The four counters against the oracle's emulation over every row
+      (1.07e9 casts): within 0.01% of each count (plus 2 threshold flips).
+    * Every output element against the emulation: at most 1% of them more
+      than 1e-4 apart.
+    * MSE against exact attention on 256 seeded rows per head: within 5% of
+      the emulation's MSE on the same rows, and below the stated MSE bound
+      (the mean squared per-element bound) there; every element of those
+      rows within its bound, checked on 8 of the heads.
+    * Forward, S=1: the flush fraction against the closed form F(Delta,S)
+      and its Monte Carlo model.  Reverse, S=256: no flush outside the sink
+      tiles."""
     need_gpu()
     c = fagen.WORKLOADS["pcast_sink_f32"]
     B, H, N, d = c["B"], c["H"], c["Nq"], c["d"]
     q, k, v = fagen.sink_inputs(0, B, H, N, d, delta)
-    rows = np.stack([np.unique(np.concatenate([[0, N - 1], fagen.sample_rows(0, h, N, 14)]))
+    rows = np.stack([np.unique(np.concatenate([[0, N - 1], fagen.sample_rows(0, h, N, 254)]))
                      for h in range(H)])
+    width = min(len(r) for r in rows)
+    rows = rows[:, :width]
+    assert width >= 255
     o_ex, _ = oracle.attention(q, k, v, True, c["scale"], rows=rows)
     d4 = oracle.expected_max_gauss(4)
     tile = fa.kv_tile(torch.float32, d, pcast=True)
@@ -105,17 +132,26 @@ def test_pcast_sink_workload_full_size(delta):
     for name, (S, rev) in (("fwd1", (1.0, False)), ("rev256", (256.0, True))):
         announce(f"fa_fwd_pcast config5 delta={delta} S={S} reverse={rev}")
         o, _, cnt, scale = _run_pair(q, k, v, S, rev, 4)
-        og = np.stack([o[0, h, rows[h]] for h in range(H)])[None]
-        oe, _, _ = oracle.pcast_emulate(q, k, v, True, scale, tile, S, rev, 4, rows=rows)
+        oe, _, ce = oracle.pcast_emulate(q, k, v, True, scale, tile, S, rev, 4)
+        announce(f"  counts gpu {cnt} emulation {ce}")
+        assert _counts_match(cnt, ce), (delta, name, cnt, ce)
+        far = float(np.mean(np.abs(o - oe) > 1e-4))
+        assert far <= 0.01, (delta, name, far)
+        sel = np.arange(H)[:, None], rows
+        og, oes = o[0][sel][None], oe[0][sel][None]
+        del o, oe
         mse[name] = float(np.mean((og - o_ex) ** 2))
-        mse_e = float(np.mean((oe - o_ex) ** 2))
+        mse_e = float(np.mean((oes - o_ex) ** 2))
         assert abs(mse[name] - mse_e) <= 0.05 * mse_e, (name, mse[name], mse_e)
-        bnd_sq = []
-        for h in range(0, H, 8):
-            a = np.stack([oracle.attention_probs(q, k, True, scale, 0, h, int(i)) for i in rows[h]])
-            bnd = pcast_bound(a, v[0, h], S)
-            assert np.all(np.abs(og[0, h] - o_ex[0, h]) <= bnd), (name, h)
-            bnd_sq.append(np.mean(bnd ** 2))
+        bnd_sq = 0.0
+        for h in range(H):
+            bnd = oracle.pcast_bound_rows(q, k, v, True, scale, S, 0, h, rows[h])
+            if h % 4 == 0:
+                assert np.all(np.abs(og[0, h] - o_ex[0, h]) <= bnd), (name, h)
+            bnd_sq += float(np.sum(bnd ** 2))
+        mse_bound = bnd_sq / og.size
+        announce(f"  mse gpu {mse[name]:.4g} emulation {mse_e:.4g} stated bound {mse_bound:.4g}")
+        assert mse[name] <= mse_bound, (name, mse[name], mse_bound)
         frac = cnt[1] / cnt[0]
         if name == "fwd1":
             F = oracle.F_closed_form(delta, S, d4)
