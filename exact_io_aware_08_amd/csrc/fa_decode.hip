@@ -21,7 +21,12 @@
 // KV head once and reuse it).  The work is a scan of the KV cache, bound by
 // HBM bandwidth, so the kernel is built to keep many bytes in flight: each
 // wave holds a ring of NP register stages and issues the loads of step
-// st + NP as soon as step st is consumed.  Loads go through buffer
+// st + NP as soon as step st is consumed.  A contiguous cache of at least
+// kStreamBytes is read with the non-temporal cache policy: measured on
+// MI355X, that is 11% faster for the 134 MB TinyLlama-shaped cache read cold
+// and 2% faster even when the same cache is read by every call, while a
+// 33 MB cache read by every call is 10% faster with the default policy (its
+// lines stay in the 256 MB last-level cache between calls).  Loads go through buffer
 // descriptors that cover exactly the workgroup's key slice, so the
 // prefetches past its end read zero and touch no memory.
 //
@@ -56,6 +61,7 @@ namespace {
 
 constexpr int NW = 4;
 constexpr int WK = 32;                    // keys per wave per step
+constexpr double kStreamBytes = 64.0 * (1 << 20);  // K + V bytes from which loads stream
 static_assert(NW * WK == kDecodeStep, "step");
 
 template <int D> struct DecodeGeo {
@@ -141,7 +147,7 @@ __device__ bool paged_auto_pair(const int *__restrict__ lens, int B, int cap, in
     return false;
 }
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool STREAM>
 __global__ void __launch_bounds__(256)
 decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__restrict__ V,
               T *__restrict__ O, float *__restrict__ LSE, float *__restrict__ part_o,
@@ -152,6 +158,7 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     using v8 = typename M::v8;
     using Geo = DecodeGeo<D>;
     constexpr int NP = Geo::NP, KT = Geo::KT, CPR = Geo::CPR, VCH = Geo::VCH, VS = Geo::VS;
+    constexpr int kPolicy = STREAM ? kLoadStream : 0;  // cache policy of the K/V loads
 
     // Per-wave V slices and the end-of-sweep merge buffer are never live
     // together, so they share one LDS block (a barrier separates the uses).
@@ -257,10 +264,10 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int t = 0; t < KT; ++t)
-                kreg[sp][kb][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[kb][t], 0, 0);
+                kreg[sp][kb][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[kb][t], 0, kPolicy);
 #pragma unroll
         for (int u = 0; u < VCH; ++u)
-            vreg[sp][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, 0);
+            vreg[sp][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, kPolicy);
         // keep the stages' loads in issue order, so the wait for the oldest
         // stage leaves the younger ones in flight
         __builtin_amdgcn_sched_barrier(0);
@@ -487,18 +494,19 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
                                          : (unsigned)p.splits * (unsigned)(p.B * hq);
     const PagedCache pc{p.block_table, p.seq_lens, p.page_size, p.max_pages, p.num_pages,
                         auto_split ? 1 : 0, p.B, auto_split ? p.split_counts : nullptr};
-    if (p.block_table != nullptr)
-        hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3(n_blocks), dim3(256), 0, st,
-                           static_cast<const T *>(p.q), static_cast<const T *>(p.k),
-                           static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.part_o,
-                           p.part_lse, p.H, p.Hkv, p.Nk, G, n_qgroups, p.splits, p.chunk, p.scale,
-                           p.scale * kLog2e, pc);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3(n_blocks), dim3(256), 0, st,
-                           static_cast<const T *>(p.q), static_cast<const T *>(p.k),
-                           static_cast<const T *>(p.v), static_cast<T *>(p.o), p.lse, p.part_o,
-                           p.part_lse, p.H, p.Hkv, p.Nk, G, n_qgroups, p.splits, p.chunk, p.scale,
-                           p.scale * kLog2e, pc);
+    // stream a large contiguous cache past the caches (paged caches and small
+    // ones keep the default policy)
+    const bool stream = p.block_table == nullptr &&
+                        2.0 * p.B * p.Hkv * (double)p.Nk * D * sizeof(T) >= (double)kStreamBytes;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(256), 0, st, static_cast<const T *>(p.q),
+                           static_cast<const T *>(p.k), static_cast<const T *>(p.v),
+                           static_cast<T *>(p.o), p.lse, p.part_o, p.part_lse, p.H, p.Hkv, p.Nk, G,
+                           n_qgroups, p.splits, p.chunk, p.scale, p.scale * kLog2e, pc);
+    };
+    if (p.block_table != nullptr) go(decode_kernel<T, D, true, false>);
+    else if (stream) go(decode_kernel<T, D, false, true>);
+    else go(decode_kernel<T, D, false, false>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int BH = p.B * p.H;

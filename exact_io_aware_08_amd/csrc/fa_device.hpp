@@ -99,18 +99,26 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, dword data format (gfx9 V# word 3)
 
+// Cache-policy operand of a buffer load: the non-temporal (NT) bit, for a
+// stream read once and too large to stay cached between uses (the decode's
+// KV cache above a size threshold).
+constexpr int kLoadStream = 2;
+
 // Buffer resource over rows [j0, rows) of a row-major slice of D-element
 // rows: loads past the end read as zero (the hardware range check on the
 // VGPR offset).  All arguments are wave-uniform.
 template <typename T, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int j0)
 {
-    // 64-bit, then clamped to the 31-bit range: a slice may hold up to 2^31
-    // elements (more bytes than an int), and every load lies within a tile
-    // or two of the rebased start
-    const long long left = rows > j0 ? (long long)(rows - j0) * D * (long long)sizeof(T) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0,
-                                             (int)(left < 0x7fffffffLL ? left : 0x7fffffffLL),
+    // A slice may hold up to 2^31 elements (more bytes than an int), and
+    // every load lies within a tile or two of the rebased start, so the byte
+    // range is clamped to 31 bits.  Done in 32-bit scalar arithmetic on the
+    // row count (a 64-bit compare would run on the vector unit).
+    constexpr int kRowBytes = D * (int)sizeof(T);
+    constexpr int kMaxRows = 0x7fffffff / kRowBytes;  // rows whose bytes fit in 31 bits
+    const int left = rows > j0 ? rows - j0 : 0;
+    const int bytes = left > kMaxRows ? 0x7fffffff : left * kRowBytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base + (size_t)j0 * D), (short)0, bytes,
                                              kBufferFlags);
 }
 
