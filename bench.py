@@ -167,6 +167,74 @@ def _sweep(torch, fa, fagen, to_dev, dev):
     return res
 
 
+CEILINGS_LIB = os.path.join(ROOT, "libfa_ceilings.so")
+
+
+def _ceilings(torch, dev, read_bytes):
+    """Attainable ceilings measured in the same run (bench_ceilings.hip): a
+    16-byte streaming read of `read_bytes`, one contiguous chunk per
+    workgroup or grid-stride, at 256-4,096 workgroups and 8 or 16 loads in
+    flight per thread, rotating over four buffers so each launch reads HBM
+    (the decode's own pattern is the chunk read at 256 workgroups); dense
+    bf16 MFMA on register operands; and the prefill's per-tile MFMA/softmax
+    instruction mix on register operands (no staging, barriers or masking).
+    The nominal peaks stay the primary denominators."""
+    import ctypes
+    if not os.path.exists(CEILINGS_LIB):
+        import __graft_entry__
+        __graft_entry__.build_ceilings()
+    lib = ctypes.CDLL(CEILINGS_LIB)
+    vp, i, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.ceil_read_chunks_launch.argtypes = [vp, ll, i, i, vp, vp]
+    lib.ceil_read_stride_launch.argtypes = [vp, ll, i, i, vp, vp]
+    lib.ceil_mfma_launch.argtypes = [i, i, vp, vp]
+    lib.ceil_mfma_mix_launch.argtypes = [i, i, vp, vp]
+    st = lambda: torch.cuda.current_stream().cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel launch failed (hipError {rc})")
+
+    res = {}
+    bufs = [torch.full((read_bytes,), r + 1, dtype=torch.uint8, device=dev) for r in range(4)]
+    out = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+
+    def read_rate(fn_, grid, unroll):
+        ms = _timed(lambda k: ok(fn_(bufs[k % 4].data_ptr(), read_bytes, grid, unroll, out.data_ptr(),
+                                     st())), 200, 400, torch)
+        return {"GB/s": round(read_bytes / (ms * 1e-3) / 1e9, 1), "us_per_call": round(ms * 1e3, 2),
+                "workgroups": grid, "loads_in_flight_per_thread": unroll}
+
+    sweep = []
+    for name, fn_ in (("chunk_per_workgroup", lib.ceil_read_chunks_launch),
+                      ("grid_stride", lib.ceil_read_stride_launch)):
+        for grid in (256, 512, 1024, 2048, 4096):
+            for unroll in (8, 16):
+                r = read_rate(fn_, grid, unroll)
+                r["pattern"] = name
+                sweep.append(r)
+    dec_pat = [r for r in sweep if r["pattern"] == "chunk_per_workgroup" and r["workgroups"] == 256]
+    res["hbm_read_decode_pattern"] = dict(max(dec_pat, key=lambda r: r["GB/s"]), bytes=read_bytes)
+    res["hbm_read_best"] = dict(max(sweep, key=lambda r: r["GB/s"]), bytes=read_bytes)
+    res["hbm_read_sweep"] = [(r["pattern"], r["workgroups"], r["loads_in_flight_per_thread"], r["GB/s"])
+                             for r in sweep]
+    del bufs, out
+    fout = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    grid, iters = 512, 2000
+    flop = 16 * 2 * 32 * 32 * 16 * 4 * grid * iters      # 16 MFMAs per wave per round, 4 waves
+    ms = _timed(lambda k: ok(lib.ceil_mfma_launch(iters, grid, fout.data_ptr(), st())), 10, 20, torch,
+                queue_ahead=False)
+    res["mfma_bf16_dense"] = {"TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1),
+                              "ms_per_call": round(ms, 4), "workgroups": grid}
+    ms = _timed(lambda k: ok(lib.ceil_mfma_mix_launch(iters, grid, fout.data_ptr(), st())), 10, 20, torch,
+                queue_ahead=False)
+    res["mfma_softmax_mix"] = {
+        "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1), "ms_per_call": round(ms, 4), "workgroups": grid,
+        "mix": "per 64x32 tile per wave: 16 MFMA 32x32x16 bf16, 32 FMA, 32 exp2, 32 add, 16 bf16 pair "
+               "converts; register operands"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +252,8 @@ def main():
                          "materialised attention")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (tiny fp32, GPT-2-small prefill, P-cast sink)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the attainable-ceiling kernels (streaming read, dense MFMA, MFMA/softmax mix)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -326,6 +396,26 @@ def main():
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": us / 1e3,
                         "config": {"workload": "gqa_decode_bf16"}, "roofline": dec["roofline"]})
         out["decode"] = dec
+
+    # ---------------- attainable ceilings on this machine ----------------
+    if not args.no_ceilings:
+        ceil = _ceilings(torch, dev, 134217728)
+        out["ceilings"] = ceil
+        if "roofline" in out and out.get("config", {}).get("workload") == "trading_day_prefill_bf16":
+            mix = ceil["mfma_softmax_mix"]["TFLOP/s"]
+            out["roofline"]["vs_ceilings"] = {
+                "mfma_bf16_dense_TFLOPs": ceil["mfma_bf16_dense"]["TFLOP/s"],
+                "frac_of_dense": round(out["roofline"]["achieved_steady"] / ceil["mfma_bf16_dense"]["TFLOP/s"], 4),
+                "mfma_softmax_mix_TFLOPs": mix,
+                "frac_of_mix": round(out["roofline"]["achieved_steady"] / mix, 4),
+                "basis": "achieved_steady over each ceiling"}
+        if "decode" in out:
+            rd = ceil["hbm_read_decode_pattern"]["GB/s"]
+            rb = ceil["hbm_read_best"]["GB/s"]
+            out["decode"]["roofline"]["vs_ceilings"] = {
+                "hbm_read_decode_pattern_GBs": rd, "frac_of_decode_pattern_read": round(out["decode"]["value"] / rd, 4),
+                "hbm_read_best_GBs": rb, "frac_of_best_read": round(out["decode"]["value"] / rb, 4),
+                "basis": "decode GB/s (sweep + merge per call) over each streaming-read ceiling of the same bytes"}
 
     # ---------------- the other workloads (reported, not the step) ----------------
     if args.only == "all" and not args.no_extra:

@@ -56,3 +56,16 @@ def test_committed_summaries_name_their_kernel_source():
     for summary in ("fa_fwd_trading_day_bf16_pmc.md", "fa_decode_gqa_bf16_pmc.md"):
         txt = open(os.path.join(ROOT, "profiles", summary)).read()
         assert "source_sha256_16:" in txt and "hbm_bytes_per_launch:" in txt
+
+
+def test_ceiling_library_builds_and_exports_its_launchers():
+    """The bench's attainable-ceiling kernels (bench_ceilings.hip) build for
+    gfx950 and export the four launchers bench.py binds (no launch here)."""
+    import ctypes
+
+    import __graft_entry__
+    path = __graft_entry__.build_ceilings()
+    lib = ctypes.CDLL(path)
+    for name in ("ceil_read_chunks_launch", "ceil_read_stride_launch", "ceil_mfma_launch",
+                 "ceil_mfma_mix_launch"):
+        assert hasattr(lib, name), name
