@@ -20,7 +20,7 @@ import torch
 
 from ._lib import FA_BF16, FA_F16, FA_F32, FaError, check, load
 
-__all__ = ["fwd", "fwd_pcast", "decode", "cast_e4m3", "kv_tile", "decode_splits",
+__all__ = ["fwd", "fwd_pcast", "decode", "decode_noalloc", "cast_e4m3", "kv_tile", "decode_splits",
            "decode_workspace_bytes", "decode_paged_workspace_bytes", "version", "FaError", "load"]
 
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -192,6 +192,31 @@ def decode(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
                           workspace.numel() * workspace.element_size() if workspace is not None
                           else 0, _stream_ptr(stream))
     check(st, "fa_decode")
+    return o, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, scale: float | None = None, num_splits: int = 0,
+                   out=None, lse=None, return_lse: bool = True, stream=None):
+    """decode() without a workspace: the split partials live in the library's
+    static 8 MiB device scratch (fa_decode_noalloc), so the C call allocates
+    nothing.  Outputs are allocated here unless passed in.  Calls that overlap
+    on one GPU race on the shared scratch."""
+    B, H, Hkv, Nq, Nk, d = _qkv_shapes(q, k_cache, v_cache)
+    if Nq != 1:
+        raise ValueError("decode takes one query token per (batch, head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _check_out("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, 1), torch.float32, q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    st = load().fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, H, Hkv, Nk, d,
+                                  float(scale), _DT[q.dtype], int(num_splits), _stream_ptr(stream))
+    check(st, "fa_decode_noalloc")
     return o, lse
 
 

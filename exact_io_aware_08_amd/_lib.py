@@ -17,7 +17,7 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_GQA",
     5: "FA_ERR_DTYPE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_SCALE", 8: "FA_ERR_WORKSPACE",
-    9: "FA_ERR_DEVICE", 10: "FA_ERR_HIP", 11: "FA_ERR_ARG",
+    9: "FA_ERR_DEVICE", 10: "FA_ERR_HIP", 11: "FA_ERR_ARG", 12: "FA_ERR_SCRATCH",
 }
 
 _vp = ctypes.c_void_p
@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]),
+    "fa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_cast_e4m3": (_i, [_vp, _vp, _vp, _sz, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,

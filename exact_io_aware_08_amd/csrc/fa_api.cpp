@@ -227,6 +227,37 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, void *o,
+                            float *lse, int B, int H, int Hkv, int Nk, int d, float scale,
+                            fa_dtype dtype, int num_splits, void *stream)
+{
+    fa_status s = check_fwd_shape(B, H, Hkv, 1, Nk, d, scale);
+    if (s != FA_OK) return s;
+    if ((s = check_fwd_ptrs(q, k_cache, v_cache, o, lse, B, 1, Nk)) != FA_OK) return s;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (num_splits < 0 || num_splits > 4096) return FA_ERR_ARG;
+    const int splits = fa_decode_splits(B, H, Hkv, Nk, num_splits);
+    const DecodeLayout lay = decode_layout(B, H, Hkv, d, splits);
+    if (lay.total > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+    const long long blocks = (long long)splits * B * Hkv * ((H / Hkv + 15) / 16);
+    if (blocks > kMaxSlice) return FA_ERR_SHAPE;
+    if (B == 0) return FA_OK;
+    if ((s = device_status()) != FA_OK) return s;
+    fa::DecodeProblem p{};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+    p.B = B; p.H = H; p.Hkv = Hkv; p.Nk = Nk; p.d = d; p.scale = scale; p.dtype = (int)dtype;
+    p.splits = splits;
+    p.chunk = decode_chunk(Nk, splits, d);
+    if (lay.total > 0) {
+        void *ws = nullptr;
+        if (fa::decode_scratch(&ws) != hipSuccess || ws == nullptr) return FA_ERR_HIP;
+        char *base = static_cast<char *>(ws);
+        p.part_lse = reinterpret_cast<float *>(base + lay.lse_off);
+        p.part_o = reinterpret_cast<float *>(base + lay.o_off);
+    }
+    return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                           const int *block_table, const int *seq_lens, void *o, float *lse,
                           int B, int H, int Hkv, int num_pages, int page_size, int max_pages,
@@ -400,6 +431,9 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_DEVICE: return "FA_ERR_DEVICE: the current device is not gfx950";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
     case FA_ERR_ARG: return "FA_ERR_ARG: an argument is out of range";
+    case FA_ERR_SCRATCH:
+        return "FA_ERR_SCRATCH: the partial results need more than the library's 8 MiB static "
+               "decode scratch (fa_decode_noalloc); use fa_decode with a workspace";
     }
     return "unknown fa_status";
 }

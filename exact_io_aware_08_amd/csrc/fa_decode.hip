@@ -53,6 +53,8 @@
 // all) and finds its (sequence, split) pair with a prefix sum over the
 // lanes, so a ragged or skewed batch fills the GPU instead of following its
 // longest sequence.
+#include <mutex>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -523,7 +525,33 @@ hipError_t launch_dt(const DecodeProblem &p, hipStream_t st)
     return p.d == 64 ? launch_t<T, 64>(p, st) : launch_t<T, 128>(p, st);
 }
 
+// Scratch of fa_decode_noalloc: the per-split partials (the workspace of
+// fa_decode) in a static device array, so that entry point allocates
+// nothing.  Each GPU holds its own copy for the life of the process.  In host
+// code the array's name is only a stand-in for the symbol: its device address
+// comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
 }  // namespace
+
+hipError_t decode_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static void *addr[kMaxDevices];
+    static hipError_t err[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev]() {
+        void *p = nullptr;
+        err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        addr[dev] = err[dev] == hipSuccess ? p : nullptr;
+    });
+    *ptr = addr[dev];
+    return err[dev];
+}
 
 int decode_chunk_keys(int d) { return kDecodeStep * (d == 64 ? DecodeGeo<64>::NP : DecodeGeo<128>::NP); }
 

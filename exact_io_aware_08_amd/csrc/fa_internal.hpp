@@ -115,6 +115,11 @@ inline long long paged_auto_pairs(int B, int hq, int smax)
     return a < b ? a : b;
 }
 
+// Static device scratch of fa_decode_noalloc (the split partials), per GPU.
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+// Device address of the current device's scratch (looked up once per device).
+hipError_t decode_scratch(void **ptr);
+
 int fwd_f32_kv_tile(int d);   // keys per KV tile, fp32 / P-cast kernel
 int fwd_mfma_kv_tile(int d, long long B, long long H, long long Nq);  // keys per KV tile, bf16 / fp16 kernel
 int decode_chunk_keys(int d); // granularity of a decode split (keys)

@@ -68,7 +68,8 @@ typedef enum {
     FA_ERR_WORKSPACE = 8, /* decode workspace NULL or too small                  */
     FA_ERR_DEVICE = 9,    /* current device is not gfx950 (or cannot be queried) */
     FA_ERR_HIP = 10,      /* a kernel launch failed                              */
-    FA_ERR_ARG = 11       /* another argument out of range                       */
+    FA_ERR_ARG = 11,      /* another argument out of range                       */
+    FA_ERR_SCRATCH = 12   /* fa_decode_noalloc: partials exceed the static scratch */
 } fa_status;
 
 /*
@@ -166,6 +167,28 @@ fa_status fa_decode(const void *q, const void *k_cache, const void *v_cache, voi
                     float *lse, int B, int H, int Hkv, int Nk, int d, float scale,
                     fa_dtype dtype, int num_splits, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * fa_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid allocation.  Same arguments, kernels and results as fa_decode
+ * (bit for bit, for the same num_splits), except that the per-split partials
+ * live in the library's own static device scratch of 8 MiB per GPU (a
+ * file-scope device array, held by each GPU the library runs on until the
+ * process ends).  The call allocates nothing; the caller passes inputs and
+ * outputs.
+ *   Limit: fa_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits) must be at
+ *   most 8 MiB (8,388,608 bytes), else FA_ERR_SCRATCH and nothing is
+ *   launched (the TinyLlama-shaped B=16, H=32, Hkv=4, Nk=8192 decode needs
+ *   0.53 MB).  A call with one split uses no scratch.
+ *   The scratch keeps whatever the last call wrote; each call's merge reads
+ *   only partials its own sweep wrote on the same stream, so nothing needs
+ *   clearing.  Every call on a GPU shares that GPU's scratch: calls that
+ *   overlap on one GPU (other streams, other host threads) race.
+ */
+fa_status fa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, void *o,
+                            float *lse, int B, int H, int Hkv, int Nk, int d, float scale,
+                            fa_dtype dtype, int num_splits, void *stream);
 
 /*
  * Split-KV decode against a paged KV cache with per-sequence lengths (the

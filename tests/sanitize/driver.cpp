@@ -83,6 +83,15 @@ int main()
           FA_ERR_ARG);
     CHECK(fa_decode(P, P, P, P, PF, 2, 8, 2, 100, 64, 0.125f, FA_F32, 3, P, ws, nullptr) ==
           FA_ERR_DTYPE);
+    // no-alloc decode: validation as fa_decode, then the static-scratch limit
+    CHECK(fa_decode_noalloc(P, P, P, P, PF, 16, 32, 4, 8192, 64, 0.125f, FA_BF16, 0, nullptr) ==
+          FA_ERR_DEVICE);
+    CHECK(fa_decode_noalloc(P, P, P, P, PF, 64, 64, 8, 1 << 20, 128, 0.125f, FA_BF16, 64, nullptr) ==
+          FA_ERR_SCRATCH);
+    CHECK(fa_decode_noalloc(P, P, P, P, PF, 2, 8, 3, 100, 64, 0.125f, FA_BF16, 0, nullptr) == FA_ERR_GQA);
+    CHECK(fa_decode_noalloc(nullptr, P, P, P, PF, 2, 8, 2, 100, 64, 0.125f, FA_BF16, 0, nullptr) ==
+          FA_ERR_NULL);
+    CHECK(fa_decode_noalloc(P, P, P, P, PF, 0, 8, 2, 100, 64, 0.125f, FA_BF16, 0, nullptr) == FA_OK);
     const int *PI = static_cast<const int *>(P);
     CHECK(fa_decode_paged(P, P, P, PI, PI, P, PF, 2, 8, 2, 16, 128, 8, 64, 0.125f, FA_BF16, 0, P,
                           fa_decode_paged_workspace_bytes(2, 8, 2, 8, 128, 64, 0), nullptr) == FA_ERR_DEVICE);

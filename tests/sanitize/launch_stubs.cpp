@@ -31,4 +31,5 @@ hipError_t launch_bwd(const BwdProblem &, hipStream_t) { std::abort(); }
 hipError_t launch_quant(const QuantProblem &, hipStream_t) { std::abort(); }
 hipError_t launch_fwd_fp8(const Fp8Problem &, hipStream_t) { std::abort(); }
 hipError_t launch_cast_e4m3(const float *, uint8_t *, float *, size_t, hipStream_t) { std::abort(); }
+hipError_t decode_scratch(void **) { std::abort(); }
 }  // namespace fa

@@ -139,6 +139,31 @@ def test_decode_split_policy_and_workspace():
     assert fa.decode_workspace_bytes(2, 8, 2, 100, 64, 1) == 0
 
 
+def test_decode_noalloc_validation_and_limit():
+    """fa_decode_noalloc validates like fa_decode, then rejects partials larger
+    than its 8 MiB static scratch with FA_ERR_SCRATCH (before any launch);
+    sizes within it reach the device check."""
+    lib = fa.load()
+
+    def call(B, H, Hkv, Nk, d, splits=0, dtype=BF16, q=P):
+        return lib.fa_decode_noalloc(q, P, P, P, P, B, H, Hkv, Nk, d, 0.125, dtype, splits, None)
+
+    assert fa.decode_workspace_bytes(16, 32, 4, 8192, 64) <= 8 << 20
+    assert call(16, 32, 4, 8192, 64) == S["FA_ERR_DEVICE"]
+    big = (64, 64, 8, 1 << 20, 128, 64)
+    assert fa.decode_workspace_bytes(*big) > 8 << 20
+    assert call(*big) == S["FA_ERR_SCRATCH"]
+    # just over and just under the limit: rows * (4 + 4d) bytes plus alignment
+    assert call(8, 16, 16, 1 << 20, 128, 2) == S["FA_ERR_DEVICE"]          # 132 KB of partials
+    assert call(1, 8, 8, 1 << 22, 128, 2048) == S["FA_ERR_SCRATCH"]        # 8.5 MB
+    assert call(2, 8, 3, 100, 64) == S["FA_ERR_GQA"]
+    assert call(2, 8, 2, 100, 64, q=None) == S["FA_ERR_NULL"]
+    assert call(2, 8, 2, 100, 64, dtype=F32) == S["FA_ERR_DTYPE"]
+    assert call(2, 8, 2, 100, 64, splits=5000) == S["FA_ERR_ARG"]
+    assert call(0, 8, 2, 100, 64) == S["FA_OK"]
+    assert "static" in lib.fa_status_str(12).decode()
+
+
 def test_kv_tile_and_cast_validation():
     assert fa.kv_tile(__import__("torch").bfloat16, 64) in (32, 64)
     lib = fa.load()
