@@ -485,6 +485,77 @@ decode_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ 
     if (LSE != nullptr && lane == 0) LSE[bh] = (M_ == -INFINITY) ? -INFINITY : M_ + logf(L);
 }
 
+// Merge for many splits (more than kMergeNarrow): one round of vector loads
+// per JB partials -- lane j reads the LSE of split s0 + j, and every lane
+// reads its output columns of all JB partial rows -- instead of scalar loads
+// that depend on each other.  The split weights reach every lane by readlane;
+// a further round (more than JB splits) folds in with a running reference
+// M_, rescaling what is already summed by e^(M_old - M_new).
+constexpr int kMergeNarrow = 16;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+decode_merge_wide_kernel(const float *__restrict__ part_o, const float *__restrict__ part_lse,
+                         T *__restrict__ O, float *__restrict__ LSE, int BH, int splits,
+                         const int *__restrict__ seq_lens, int H, int chunk, int cap,
+                         const int *__restrict__ split_counts)
+{
+    constexpr int DPL = D / 64;    // output columns per lane
+    constexpr int JB = 64 / DPL;   // partial rows per round of loads
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (bh >= BH) return;
+    int nsp = splits;
+    if (split_counts != nullptr) {
+        nsp = max(1, min(splits, split_counts[bh / H]));
+    } else if (seq_lens != nullptr) {
+        const int len = max(0, min(seq_lens[bh / H], cap));
+        nsp = max(1, min(splits, (len + chunk - 1) / chunk));
+    }
+    const float *pl = part_lse + (size_t)bh * splits;
+    const float *po = part_o + (size_t)bh * splits * D + lane;
+
+    float M_ = -INFINITY, L = 0.f, acc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < nsp; s0 += JB) {
+        const int n = min(JB, nsp - s0);
+        const float lj = lane < n ? pl[s0 + lane] : -INFINITY;
+        float vb[JB][DPL];
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const int sj = s0 + min(j, n - 1);
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) vb[j][i] = po[(size_t)sj * D + 64 * i];
+        }
+        float mb = lj;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+        const float Mn = fmaxf(M_, mb);
+        if (Mn == -INFINITY) continue;  // every split so far empty (wave-uniform)
+        const float a = fast_exp2((M_ - Mn) * kLog2e);  // 0 while M_ = -inf
+        L *= a;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] *= a;
+        const float wl = lane < n ? fast_exp2((lj - Mn) * kLog2e) : 0.f;
+        float ws = wl;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
+        L += ws;
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) acc[i] += wj * vb[j][i];
+        }
+        M_ = Mn;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) O[(size_t)bh * D + lane + 64 * i] = static_cast<T>(acc[i] * inv);
+    if (LSE != nullptr && lane == 0) LSE[bh] = (M_ == -INFINITY) ? -INFINITY : M_ + logf(L);
+}
+
 template <typename T, int D>
 hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
 {
@@ -512,8 +583,9 @@ hipError_t launch_t(const DecodeProblem &p, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int BH = p.B * p.H;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0,
-                       st, p.part_o, p.part_lse, static_cast<T *>(p.o), p.lse, BH, p.splits,
+    auto merge = p.splits > kMergeNarrow ? decode_merge_wide_kernel<T, D> : decode_merge_kernel<T, D>;
+    hipLaunchKernelGGL(merge, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, st, p.part_o,
+                       p.part_lse, static_cast<T *>(p.o), p.lse, BH, p.splits,
                        p.block_table != nullptr ? p.seq_lens : nullptr, p.H, p.chunk,
                        p.max_pages * p.page_size, auto_split ? p.split_counts : nullptr);
     return hipGetLastError();

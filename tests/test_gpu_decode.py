@@ -39,6 +39,22 @@ def test_tinyllama_gqa_decode_bf16():
     run_decode(16, 32, 4, 8192, 64, "bf16")
 
 
+def test_single_sequence_gqa_decode():
+    """B=1, 32 query heads / 4 KV heads, 65,536 keys, d=64, bf16: B*Hkv = 4,
+    so the automatic policy cuts each KV head into 64 splits and the merge
+    takes its many-split path (one round of loads per 64 partials)."""
+    assert fa.decode_splits(1, 32, 4, 65536) == 64
+    run_decode(1, 32, 4, 65536, 64, "bf16", seed=5, poison_ws=True)
+
+
+@pytest.mark.parametrize("splits", [17, 100, 257])
+def test_many_split_merge(splits):
+    """Split counts above 16 take the many-split merge, including more than
+    one round of 64 partials (100, 257) and empty trailing splits."""
+    run_decode(1, 8, 2, 30000, 64, "bf16", splits=splits, seed=splits, poison_ws=True)
+    run_decode(1, 4, 1, 20000, 128, "f16", splits=splits, seed=splits + 1, poison_ws=True)
+
+
 @pytest.mark.parametrize("splits", [1, 3, 16, 64])
 def test_split_counts(splits):
     run_decode(2, 8, 2, 3000, 64, "bf16", splits=splits, seed=splits, poison_ws=True)
