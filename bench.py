@@ -40,9 +40,20 @@ PREFILL_KERNEL = "exact_io_aware_08_amd/csrc/fa_fwd_mfma.hip"
 DECODE_KERNEL = "exact_io_aware_08_amd/csrc/fa_decode.hip"
 
 
+# headers every kernel source includes: a change there changes the kernel too
+KERNEL_HEADERS = ("exact_io_aware_08_amd/csrc/fa_device.hpp", "exact_io_aware_08_amd/csrc/fa_internal.hpp")
+
+
 def _sha(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 prefix of a kernel source followed by the headers it includes
+    (those that exist under ROOT), the hash a profile summary records."""
+    h = hashlib.sha256()
+    for p in (path,) + KERNEL_HEADERS:
+        full = os.path.join(ROOT, p)
+        if os.path.exists(full):
+            with open(full, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(summary, kernel_src):
@@ -170,7 +181,7 @@ def _sweep(torch, fa, fagen, to_dev, dev):
 CEILINGS_LIB = os.path.join(ROOT, "libfa_ceilings.so")
 
 
-def _ceilings(torch, dev, read_bytes):
+def _ceilings(torch, dev, read_bytes, calls=200):
     """Attainable ceilings measured in the same run (bench_ceilings.hip): a
     16-byte streaming read of `read_bytes`, one contiguous chunk per
     workgroup or grid-stride, at 256-4,096 workgroups and 8 or 16 loads in
@@ -201,7 +212,7 @@ def _ceilings(torch, dev, read_bytes):
 
     def read_rate(fn_, grid, unroll):
         ms = _timed(lambda k: ok(fn_(bufs[k % 4].data_ptr(), read_bytes, grid, unroll, out.data_ptr(),
-                                     st())), 200, 400, torch)
+                                     st())), calls, 2 * calls, torch)
         return {"GB/s": round(read_bytes / (ms * 1e-3) / 1e9, 1), "us_per_call": round(ms * 1e3, 2),
                 "workgroups": grid, "loads_in_flight_per_thread": unroll}
 
@@ -252,6 +263,8 @@ def main():
                          "materialised attention")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (tiny fp32, GPT-2-small prefill, P-cast sink)")
+    ap.add_argument("--ceiling-calls", type=int, default=200,
+                    help="timed calls per streaming-read ceiling configuration (twice as many warm-up)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the attainable-ceiling kernels (streaming read, dense MFMA, MFMA/softmax mix)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -399,7 +412,7 @@ def main():
 
     # ---------------- attainable ceilings on this machine ----------------
     if not args.no_ceilings:
-        ceil = _ceilings(torch, dev, 134217728)
+        ceil = _ceilings(torch, dev, 134217728, args.ceiling_calls)
         out["ceilings"] = ceil
         if "roofline" in out and out.get("config", {}).get("workload") == "trading_day_prefill_bf16":
             mix = ceil["mfma_softmax_mix"]["TFLOP/s"]
