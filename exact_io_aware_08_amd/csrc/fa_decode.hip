@@ -245,16 +245,27 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
     const int tr0 = (4 * g + c / 4) * VS + 4 * (c % 4);
 
     u32x4_t kreg[NP][2][KT], vreg[NP][VCH];
+    // Paged: a window of the block table in one register, lane l holding the
+    // physical page of logical page tab_win + l of this sequence (read once,
+    // refreshed every 64 pages), so a stage's addresses need no dependent
+    // scalar load.  Entries past the table are clamped to its last one.
+    int tab_win = 0, tab = 0;
+    auto tab_load = [&](int first) {
+        tab_win = first;
+        tab = pc.block_table[(size_t)b * pc.max_pages + min(first + lane, pc.max_pages - 1)];
+    };
+    if (PAGED) tab_load(min(kbeg / pc.page_size, pc.max_pages - 1));
     const int nsteps = kend > kbeg ? (kend - kbeg + kDecodeStep - 1) / kDecodeStep : 0;
     auto load_step = [&](int sp, int st) {
         const int rel = st * kDecodeStep + w * WK;  // first key of this wave's 32, in the slice
         long long left = (long long)(kend - kbeg - rel) * D * (long long)sizeof(T);
         size_t row0 = (size_t)(kbeg + rel) * D;  // element offset of the block's first key
         if (PAGED) {
-            // wave-uniform: one table entry per 32-key block (scalar load)
+            // wave-uniform: one table entry per 32-key block, from the window
             const int t = kbeg + rel;
             const int pidx = min(t / pc.page_size, pc.max_pages - 1);
-            const int phys = pc.block_table[(size_t)b * pc.max_pages + pidx];
+            if (pidx - tab_win >= 64) tab_load(pidx);
+            const int phys = __builtin_amdgcn_readlane(tab, pidx - tab_win);
             const int in_page = t - pidx * pc.page_size;
             const bool ok = t < kend && (unsigned)phys < (unsigned)pc.num_pages;
             left = ok ? (long long)min(kend - t, pc.page_size - in_page) * D * (long long)sizeof(T) : 0;

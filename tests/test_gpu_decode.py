@@ -180,6 +180,27 @@ def test_paged_varlen_matches_oracle(page_size):
         compare(o_b, lse[b:b + 1], o_ref, l_ref, dt, f"paged b={b} L={L}")
 
 
+@pytest.mark.parametrize("splits", [1, 2, 3])
+def test_paged_block_table_window_refresh(splits):
+    """32-key pages and splits that span more than 64 pages: the sweep holds a
+    64-entry window of the block table per wave and refreshes it as it walks;
+    lengths end on, just past and well inside a window boundary."""
+    need_gpu()
+    B, H, Hkv, d, dt = 4, 8, 2, 64, "bf16"
+    lens = [2048, 2049, 6000, 4097]
+    announce(f"fa_decode_paged page_size=32 lens={lens} splits={splits}")
+    q, k, v, kp, vp, table, _, _ = _paged_case(B, H, Hkv, lens, 32, d, dt, seed=31 + splits)
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=0.125,
+                             num_splits=splits)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, 0.125)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, dt, f"paged window b={b} L={L}")
+
+
 @pytest.mark.parametrize("dt,d", [("f16", 64), ("bf16", 128)])
 def test_paged_dtypes_and_head_dims(dt, d):
     need_gpu()
