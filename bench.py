@@ -181,6 +181,51 @@ def _sweep(torch, fa, fagen, to_dev, dev):
 CEILINGS_LIB = os.path.join(ROOT, "libfa_ceilings.so")
 
 
+_CEIL = []
+
+
+def _ceil_lib():
+    """The ceiling kernels (bench_ceilings.hip), built in-tree if missing."""
+    if not _CEIL:
+        import ctypes
+        if not os.path.exists(CEILINGS_LIB):
+            import __graft_entry__
+            __graft_entry__.build_ceilings()
+        lib = ctypes.CDLL(CEILINGS_LIB)
+        vp, i, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+        lib.ceil_read_chunks_launch.argtypes = [vp, ll, i, i, vp, vp]
+        lib.ceil_read_stride_launch.argtypes = [vp, ll, i, i, vp, vp]
+        lib.ceil_mfma_launch.argtypes = [i, i, vp, vp]
+        lib.ceil_mfma_mix_launch.argtypes = [i, i, vp, vp]
+        lib.ceil_mfma_mix_variant_launch.argtypes = [i, i, i, vp, vp]
+        _CEIL.append(lib)
+    return _CEIL[0]
+
+
+def _ceil_ok(rc):
+    if rc != 0:
+        raise RuntimeError(f"ceiling kernel launch failed (hipError {rc})")
+
+
+def _read_ceiling(torch, dev, nbytes, grid, calls=200):
+    """Streaming-read ceiling of `nbytes` in the decode's own pattern (one
+    contiguous chunk per workgroup, `grid` workgroups), best of 8 and 16 loads
+    in flight per thread, over four rotating buffers."""
+    lib = _ceil_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    bufs = [torch.full((nbytes,), r + 1, dtype=torch.uint8, device=dev) for r in range(4)]
+    out = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    best = None
+    for unroll in (8, 16):
+        ms = _timed(lambda k: _ceil_ok(lib.ceil_read_chunks_launch(bufs[k % 4].data_ptr(), nbytes, grid, unroll,
+                                                                   out.data_ptr(), st)), calls, 2 * calls, torch)
+        if best is None or ms < best[0]:
+            best = (ms, unroll)
+    del bufs, out
+    return {"GB/s": round(nbytes / (best[0] * 1e-3) / 1e9, 1), "us_per_call": round(best[0] * 1e3, 2),
+            "workgroups": grid, "loads_in_flight_per_thread": best[1], "bytes": nbytes}
+
+
 def _ceilings(torch, dev, read_bytes, calls=200):
     """Attainable ceilings measured in the same run (bench_ceilings.hip): a
     16-byte streaming read of `read_bytes`, one contiguous chunk per
@@ -190,22 +235,9 @@ def _ceilings(torch, dev, read_bytes, calls=200):
     bf16 MFMA on register operands; and the prefill's per-tile MFMA/softmax
     instruction mix on register operands (no staging, barriers or masking).
     The nominal peaks stay the primary denominators."""
-    import ctypes
-    if not os.path.exists(CEILINGS_LIB):
-        import __graft_entry__
-        __graft_entry__.build_ceilings()
-    lib = ctypes.CDLL(CEILINGS_LIB)
-    vp, i, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
-    lib.ceil_read_chunks_launch.argtypes = [vp, ll, i, i, vp, vp]
-    lib.ceil_read_stride_launch.argtypes = [vp, ll, i, i, vp, vp]
-    lib.ceil_mfma_launch.argtypes = [i, i, vp, vp]
-    lib.ceil_mfma_mix_launch.argtypes = [i, i, vp, vp]
+    lib = _ceil_lib()
     st = lambda: torch.cuda.current_stream().cuda_stream
-
-    def ok(rc):
-        if rc != 0:
-            raise RuntimeError(f"ceiling kernel launch failed (hipError {rc})")
-
+    ok = _ceil_ok
     res = {}
     bufs = [torch.full((read_bytes,), r + 1, dtype=torch.uint8, device=dev) for r in range(4)]
     out = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
@@ -243,6 +275,18 @@ def _ceilings(torch, dev, read_bytes, calls=200):
         "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1), "ms_per_call": round(ms, 4), "workgroups": grid,
         "mix": "per 64x32 tile per wave: 16 MFMA 32x32x16 bf16, 32 FMA, 32 exp2, 32 add, 16 bf16 pair "
                "converts; register operands"}
+    # the same mix with VALU work taken out or moved to the MFMA pipe; the rate
+    # counts only the 16 MFMAs of the mix itself
+    variants = []
+    for v, name in ((0, "as the prefill (16 MFMA; 32 FMA, 32 exp2, 32 add, 16 cvt)"),
+                    (1, "no FMA"), (2, "no row-sum adds"), (3, "exp2 and cvt only"),
+                    (4, "no FMA, scores from a hi/lo split of the scaled Q (24 MFMA)"),
+                    (5, "row sums on the MFMA pipe, no adds (20 MFMA)")):
+        msv = _timed(lambda k: ok(lib.ceil_mfma_mix_variant_launch(v, iters, grid, fout.data_ptr(), st())),
+                     10, 20, torch, queue_ahead=False)
+        variants.append({"variant": name, "TFLOP/s": round(flop / (msv * 1e-3) / 1e12, 1),
+                         "ms_per_call": round(msv, 4)})
+    res["mfma_softmax_mix_variants"] = variants
     return res
 
 
@@ -473,6 +517,12 @@ def main():
                            "GB/s": round(bx / (usx * 1e-6) / 1e9, 1),
                            "frac_of_hbm_peak": round(bx / (usx * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
             del cachex, qx, wsx
+            if not args.no_ceilings:
+                # a plain read of the same K/V bytes at the sweep's own grid
+                gx = Bx * Hkvx * max(1, fa.decode_splits(Bx, Hx, Hkvx, Nkx)) * ((Hx // Hkvx + 15) // 16)
+                rc = _read_ceiling(torch, dev, 2 * Bx * Hkvx * Nkx * 64 * 2, gx, 200)
+                extra[name]["read_ceiling"] = rc
+                extra[name]["frac_of_read_ceiling"] = round(bx / (usx * 1e-6) / 1e9 / rc["GB/s"], 4)
         # backward by recomputation on the trading-day prefill (GPU forward's O, LSE)
         g3 = torch.empty_like(q3).normal_(generator=torch.Generator(device=dev).manual_seed(0))
         ws3 = torch.empty(max(fa.bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8, device=dev)

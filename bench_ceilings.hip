@@ -18,7 +18,8 @@
 //  * ceil_mfma_mix: the prefill's per-tile instruction mix with operands in
 //    registers -- 16 MFMAs against 32 FMA, 32 exp2, 32 adds and 16 bf16 pair
 //    conversions per wave, interleaved the way the prefill kernel does -- with
-//    no LDS staging, barriers, masking or causal tail: what that mix allows.
+//    no LDS staging, barriers, masking or causal tail: what that mix allows;
+//    its variants take VALU work out or move it to the MFMA pipe.
 // Every kernel stores one value per thread (or per workgroup) derived from all
 // of its work, so none of it is dead.
 #include <hip/hip_runtime.h>
@@ -113,17 +114,34 @@ ceil_mfma(int iters, float *__restrict__ out)
 // 32 values per lane) into exp2(s * c + m) with their row sums and packs them
 // to bf16 pairs that feed the next tile's P V.  Unrolled by two so the score
 // registers swap roles instead of being copied, as in the prefill kernel.
+//
+// The template flags give the trade-off variants (the default, all of FMA and
+// ADD and neither extra, is the ceiling):
+//   FMA  -- the scale-and-shift FMA before each exp2; without it the scores
+//           arrive shifted (the accumulator starts from a per-lane -m) and
+//           unscaled, i.e. the VALU work left if the scale were folded into Q;
+//   ADD  -- the row sums as fp32 adds on the VALU;
+//   XQK  -- 8 more score MFMAs: the cost of folding the scale into Q exactly,
+//           as a bf16 hi/lo split of the scaled Q (twice the score products);
+//   XSUM -- 4 more MFMAs that take the row sums from the packed P with an
+//           all-ones operand, in place of the VALU adds.
+template <bool FMA, bool ADD, bool XQK, bool XSUM>
 __global__ void __launch_bounds__(256, 2)
 ceil_mfma_mix(int iters, float c, float *__restrict__ out)
 {
     const float s0 = (float)(threadIdx.x & 63) * 0.015625f;
     bf16x8_t kop = seed_op(s0);
     const bf16x8_t qop[2] = {seed_op(1.f - s0), seed_op(0.75f - s0)};  // two query blocks
+    const bf16x8_t qlo[2] = {seed_op(0.01f - 0.001f * s0), seed_op(0.02f - 0.001f * s0)};
     const bf16x8_t vop = seed_op(0.5f * s0);
-    f32x16_t sa[2], sb[2], acc[4];
+    const bf16x8_t ones = seed_op(100.f);
+    f32x16_t sa[2], sb[2], acc[4], lsum[2];
     bf16x8_t p[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) sa[i] = f32x16_t{};
+    for (int i = 0; i < 2; ++i) {
+        sa[i] = f32x16_t{};
+        lsum[i] = f32x16_t{};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
 #pragma unroll
@@ -132,15 +150,23 @@ ceil_mfma_mix(int iters, float c, float *__restrict__ out)
         for (int t = 0; t < 2; ++t) p[i][t] = qop[i];
     float rowsum[2] = {0.f, 0.f};
     const float mneg = -0.25f;
+    // score accumulator start: 0, or a per-lane -m when the FMA is left out
+    f32x16_t cinit;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cinit[e] = FMA ? 0.f : mneg + 0.001f * s0;
+    constexpr int NM = 16 + (XQK ? 8 : 0) + (XSUM ? 4 : 0);  // MFMAs per step
+    constexpr int NV = (FMA ? 32 : 0) + 32 + (ADD ? 32 : 0) + 16;  // VALU per step
     auto step = [&](const f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         asm volatile("" : "+v"(kop));  // a new K tile every step (not loop-invariant)
-        // 8 MFMAs: next scores (2 query blocks x 4 K-steps)
+        // 8 MFMAs (16 with XQK): next scores (2 query blocks x 4 K-steps)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            sn[qb] = f32x16_t{};
+            sn[qb] = cinit;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t) {
                 sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb], sn[qb], 0, 0, 0);
+                if (XQK) sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qlo[qb], sn[qb], 0, 0, 0);
+            }
         }
         // 8 MFMAs: P V of the previous tile (2 d-blocks x 2 K-steps x 2 query blocks)
 #pragma unroll
@@ -151,6 +177,13 @@ ceil_mfma_mix(int iters, float c, float *__restrict__ out)
                 for (int qb = 0; qb < 2; ++qb)
                     acc[2 * qb + mb] =
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[qb][t], acc[2 * qb + mb], 0, 0, 0);
+        if (XSUM) {  // 4 MFMAs: row sums of the previous tile's packed P
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    lsum[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, p[qb][t], lsum[qb], 0, 0, 0);
+        }
         // softmax of the current scores: 32 FMA + 32 exp2 + 32 adds + 16 converts
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -159,9 +192,14 @@ ceil_mfma_mix(int iters, float c, float *__restrict__ out)
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * t + 2 * e], c, mneg));
-                    const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * t + 2 * e + 1], c, mneg));
-                    rowsum[qb] = rowsum[qb] + x0 + x1;
+                    float a0 = sc[qb][8 * t + 2 * e], a1 = sc[qb][8 * t + 2 * e + 1];
+                    if (FMA) {
+                        a0 = fmaf(a0, c, mneg);
+                        a1 = fmaf(a1, c, mneg);
+                    }
+                    const float x0 = __builtin_amdgcn_exp2f(a0);
+                    const float x1 = __builtin_amdgcn_exp2f(a1);
+                    if (ADD) rowsum[qb] = rowsum[qb] + x0 + x1;
                     const bf16x2_t pk = __builtin_convertvector((f32x2_t{x0, x1}), bf16x2_t);
                     w[e] = __builtin_bit_cast(uint32_t, pk);
                 }
@@ -169,8 +207,8 @@ ceil_mfma_mix(int iters, float c, float *__restrict__ out)
             }
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
 #pragma unroll
-        for (int i = 0; i < 15; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x0002, 7, 0);
+        for (int i = 0; i < NM - 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0002, NV / (NM - 1), 0);
             __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
         }
     };
@@ -182,7 +220,7 @@ ceil_mfma_mix(int iters, float c, float *__restrict__ out)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) r += acc[i][e] + sa[i & 1][e];
+        for (int e = 0; e < 16; ++e) r += acc[i][e] + sa[i & 1][e] + lsum[i & 1][e];
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
@@ -230,8 +268,31 @@ int ceil_mfma_launch(int iters, int grid, void *out, void *stream)
 
 int ceil_mfma_mix_launch(int iters, int grid, void *out, void *stream)
 {
-    hipLaunchKernelGGL(ceil_mfma_mix, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       iters, 0.125f * 1.4426950408889634f, static_cast<float *>(out));
+    hipLaunchKernelGGL((ceil_mfma_mix<true, true, false, false>), dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), iters, 0.125f * 1.4426950408889634f,
+                       static_cast<float *>(out));
+    return (int)hipGetLastError();
+}
+
+// The trade-off variants of the mix (0 is the ceiling itself):
+// 0 as the prefill; 1 no FMA; 2 no row-sum adds; 3 exp2 and converts only;
+// 4 no FMA, scores from a hi/lo split of the scaled Q (24 MFMAs);
+// 5 row sums on the MFMA pipe instead of the VALU (20 MFMAs).
+// Returns hipErrorInvalidValue (1) for another variant.
+int ceil_mfma_mix_variant_launch(int variant, int iters, int grid, void *out, void *stream)
+{
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const float c = 0.125f * 1.4426950408889634f;
+    float *o = static_cast<float *>(out);
+    switch (variant) {
+    case 0: hipLaunchKernelGGL((ceil_mfma_mix<true, true, false, false>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    case 1: hipLaunchKernelGGL((ceil_mfma_mix<false, true, false, false>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    case 2: hipLaunchKernelGGL((ceil_mfma_mix<true, false, false, false>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    case 3: hipLaunchKernelGGL((ceil_mfma_mix<false, false, false, false>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    case 4: hipLaunchKernelGGL((ceil_mfma_mix<false, true, true, false>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    case 5: hipLaunchKernelGGL((ceil_mfma_mix<true, false, false, true>), dim3(grid), dim3(256), 0, st, iters, c, o); break;
+    default: return (int)hipErrorInvalidValue;
+    }
     return (int)hipGetLastError();
 }
 

@@ -60,12 +60,12 @@ def test_committed_summaries_name_their_kernel_source():
 
 def test_ceiling_library_builds_and_exports_its_launchers():
     """The bench's attainable-ceiling kernels (bench_ceilings.hip) build for
-    gfx950 and export the four launchers bench.py binds (no launch here)."""
+    gfx950 and export the launchers bench.py binds (no launch here)."""
     import ctypes
 
     import __graft_entry__
     path = __graft_entry__.build_ceilings()
     lib = ctypes.CDLL(path)
     for name in ("ceil_read_chunks_launch", "ceil_read_stride_launch", "ceil_mfma_launch",
-                 "ceil_mfma_mix_launch"):
+                 "ceil_mfma_mix_launch", "ceil_mfma_mix_variant_launch"):
         assert hasattr(lib, name), name
