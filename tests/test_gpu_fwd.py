@@ -168,6 +168,20 @@ def test_lse_optional_and_stream():
     compare(o, None, o_ref, None, "bf16", "side stream")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk", [(2, 4, 2, 1500, 1500), (1, 3, 1, 640, 1000),
+                                           (1, 2, 2, 1000, 640), (3, 2, 1, 64, 64),
+                                           (1, 2, 1, 130, 130)])
+def test_small_causal_grid_all_rows(dt, B, H, Hkv, Nq, Nk):
+    """Small causal grids (fewer than 1,024 workgroups of 256 rows) run
+    128-row workgroups with 64-key tiles.  Shapes give odd and even tile
+    counts per workgroup, rows that see no key (Nq > Nk), GQA and ragged last
+    tiles; every row of every head is compared, bf16 and fp16."""
+    assert -(-Nq // 256) * B * H < 1024
+    m = run_case(B, H, Hkv, Nq, Nk, 64, dt, True, seed=Nq + 3 * Nk + B + (dt == "f16"))
+    announce(f"  small causal grid {dt} {B}x{H}/{Hkv} {Nq}x{Nk}: {m}")
+
+
 @pytest.mark.parametrize("dt,causal", [("bf16", True), ("bf16", False), ("f16", True),
                                        ("f16", False)])
 def test_large_grid_uses_256_row_tiles(dt, causal):
