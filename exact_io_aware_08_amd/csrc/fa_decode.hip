@@ -149,8 +149,25 @@ __device__ bool paged_auto_pair(const int *__restrict__ lens, int B, int cap, in
     return false;
 }
 
+// Max over the lanes l and l^16 (resp. l^32): the four 16-lane groups of a
+// wave hold the same query heads for different keys.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// (Two workgroups per CU as the register target: the kernel then fits in
+// 256 VGPRs with no accumulation registers, where a one-workgroup target let
+// the compiler park the MFMA results in AGPRs and copy them to and from the
+// VGPRs every step.)
 template <typename T, int D, bool PAGED, bool STREAM>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__restrict__ V,
               T *__restrict__ O, float *__restrict__ LSE, float *__restrict__ part_o,
               float *__restrict__ part_lse, int H, int Hkv, int Nk, int G, int n_qgroups,
@@ -335,12 +352,19 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s[kb][q]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_xor16(mx);
+            mx = max_xor32(mx);
             const float m_new = fmaxf(m_run, mx);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2((m_run - m_use) * scale_log2);
             const float mneg = -m_use * scale_log2;
+            // Rescale only when some row's max moved: otherwise alpha is
+            // exactly 1, and after the first steps the max rarely moves.
+            float alpha = 1.f;
+            if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+                alpha = fast_exp2((m_run - m_use) * scale_log2);
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+            }
             float rs = 0.f;
             v8 pop;
 #pragma unroll
@@ -353,8 +377,6 @@ decode_kernel(const T *__restrict__ Qg, const T *__restrict__ K, const T *__rest
                 }
             l_run = l_run * alpha + rs;
             m_run = m_new;
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
 
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
