@@ -664,10 +664,14 @@ def main():
         nthr = oracle.default_threads()
         HS = 4  # heads of the emulated slice
         tile5 = fa.kv_tile(torch.float32, d5, pcast=True)
+        t_exact = t_emul = 0.0  # oracle time: exact attention on the sampled rows, emulation runs
+        n_emul = 0
         for delta in c5["deltas"]:
             k5n_d = k5n.copy()
             k5n_d[:, :, :4, 0] += np.float32(delta * math.sqrt(d5))
+            t0 = time.perf_counter()
             o_ex, _ = oracle.attention(q5n, k5n_d, v5n, True, c5["scale"], rows=rows5, nthreads=nthr)
+            t_exact += time.perf_counter() - t0
             probs = [np.stack([oracle.attention_probs(q5n, k5n_d, True, c5["scale"], 0, h, int(i))
                                for i in rows5[h]]) for h in range(H5)]
             k5d = to_dev(k5n_d, "f32")
@@ -686,8 +690,11 @@ def main():
                 _, _, cs = fa.fwd_pcast(qs, ks, vs, causal=True, scale=c5["scale"], p_scale=S,
                                         kv_reverse=rev, n_sink=4)
                 cs = [int(x) for x in cs.cpu()]
+                t0 = time.perf_counter()
                 _, _, ce = oracle.pcast_emulate(q5n[:, :HS], k5n_d[:, :HS], v5n[:, :HS], True,
                                                 c5["scale"], tile5, S, rev, 4, nthreads=nthr)
+                t_emul += time.perf_counter() - t0
+                n_emul += 1
                 r["heads_0_3"] = {
                     "gpu": {"casts": cs[0], "flushed": cs[1], "flushed_outside_sink_tiles": cs[3]},
                     "emulation": {"casts": ce[0], "flushed": ce[1], "flushed_outside_sink_tiles": ce[3],
@@ -700,6 +707,19 @@ def main():
         out["other_workloads"]["pcast_sink_f32"]["emulation_sample"] = (
             "oracle emulation over every row of heads 0-3 (1/8 of the workload), beside the GPU "
             "counters of a run on the same four heads")
+        if "cpu_baseline" in out:
+            # the oracle's own time on this workload: exact attention on the sampled rows, and
+            # the P-cast emulation of heads 0-3 per (Delta, run)
+            ex_pairs = len(c5["deltas"]) * float((rows5 + 1).sum())
+            em_pairs = n_emul * HS * N5 * (N5 + 1) / 2
+            out["cpu_baseline"].setdefault("other_configs", {})["pcast_sink_f32"] = {
+                "exact_sampled_seconds": round(t_exact, 3),
+                "exact_sampled_pairs_per_s": round(ex_pairs / t_exact, 1),
+                "emulation_runs": n_emul, "emulation_seconds": round(t_emul, 3),
+                "emulation_pairs_per_s": round(em_pairs / t_emul, 1),
+                "emulation_gflops_fp32_equiv": round(4.0 * d5 * em_pairs / t_emul / 1e9, 3),
+                "sample": f"exact: 32 rows per head x {H5} heads per Delta; emulation: every row of "
+                          f"heads 0-{HS - 1} per (Delta, run)"}
         # the page's own setting: N = 4096, MSE of each cast setting against exact attention
         N6 = 4096
         rows6 = np.stack([fagen.sample_rows(2, h, N6, 8) for h in range(H5)])
