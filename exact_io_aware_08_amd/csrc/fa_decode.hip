@@ -100,97 +100,6 @@ struct PagedCache {
     int *split_counts;  // automatic splits with a merge: [B], each sequence's split count
 };
 
-// Cross-lane steps within a wave of 64 without LDS: DPP row operations
-// (quad_perm, row_half_mirror, row_mirror, row_shr, row_bcast) and the
-// permlane swaps.  The reduction pairs lane l with l^1 and l^2 (quad_perm),
-// then with 7 - l within each 8 (half mirror: the other quad), 15 - l within
-// each 16 (mirror: the other half row), l^16 and l^32; each step combines two
-// disjoint partial results symmetrically, so every lane ends with the same
-// full reduction.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ int dpp_mov(int x)
-{
-    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, true);
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm (1,0,3,2)
-constexpr int kDppXor2 = 0x4E;        // quad_perm (2,3,0,1)
-constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
-constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
-constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
-constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
-
-// The two values of a permlane swap of x with itself: {x[l], x[l^16]} or
-// {x[l^16], x[l]} (resp. l^32), in the same order in both lanes of a pair.
-__device__ __forceinline__ void pair16(int x, int &a, int &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    a = (int)r[0];
-    b = (int)r[1];
-}
-__device__ __forceinline__ void pair32(int x, int &a, int &b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    a = (int)r[0];
-    b = (int)r[1];
-}
-
-template <typename Op>
-__device__ __forceinline__ float wave_reduce_f32(float x, Op op)
-{
-    x = op(x, __int_as_float(dpp_mov<kDppXor1>(__float_as_int(x))));
-    x = op(x, __int_as_float(dpp_mov<kDppXor2>(__float_as_int(x))));
-    x = op(x, __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(x))));
-    x = op(x, __int_as_float(dpp_mov<kDppMirror>(__float_as_int(x))));
-    int a, b;
-    pair16(__float_as_int(x), a, b);
-    x = op(__int_as_float(a), __int_as_float(b));
-    pair32(__float_as_int(x), a, b);
-    return op(__int_as_float(a), __int_as_float(b));
-}
-__device__ __forceinline__ float wave_sum_f32(float x)
-{
-    return wave_reduce_f32(x, [](float u, float v) { return u + v; });
-}
-__device__ __forceinline__ float wave_max_f32(float x)
-{
-    return wave_reduce_f32(x, [](float u, float v) { return fmaxf(u, v); });
-}
-
-// Sum over the wave of a 64-bit integer (the halves move separately).
-__device__ __forceinline__ long long wave_sum_i64(long long x)
-{
-    auto step = [](long long v, int lo, int hi) {
-        return v + (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-    };
-    x = step(x, dpp_mov<kDppXor1>((int)x), dpp_mov<kDppXor1>((int)(x >> 32)));
-    x = step(x, dpp_mov<kDppXor2>((int)x), dpp_mov<kDppXor2>((int)(x >> 32)));
-    x = step(x, dpp_mov<kDppHalfMirror>((int)x), dpp_mov<kDppHalfMirror>((int)(x >> 32)));
-    x = step(x, dpp_mov<kDppMirror>((int)x), dpp_mov<kDppMirror>((int)(x >> 32)));
-    int a0, b0, a1, b1;
-    pair16((int)x, a0, b0);
-    pair16((int)(x >> 32), a1, b1);
-    x = (long long)(((unsigned long long)(unsigned)a1 << 32) | (unsigned)a0) +
-        (long long)(((unsigned long long)(unsigned)b1 << 32) | (unsigned)b0);
-    pair32((int)x, a0, b0);
-    pair32((int)(x >> 32), a1, b1);
-    return (long long)(((unsigned long long)(unsigned)a1 << 32) | (unsigned)a0) +
-           (long long)(((unsigned long long)(unsigned)b1 << 32) | (unsigned)b0);
-}
-
-// Inclusive prefix sum over the 64 lanes: scans within 16-lane rows, then
-// row 0's total into row 1 and row 2's into row 3, then rows 0-1's total
-// into rows 2-3.
-__device__ __forceinline__ int wave_scan_i32(int x)
-{
-    x += dpp_mov<kDppShr1>(x);
-    x += dpp_mov<kDppShr2>(x);
-    x += dpp_mov<kDppShr4>(x);
-    x += dpp_mov<kDppShr8>(x);
-    x += dpp_mov<kDppBcast15, 0xA>(x);
-    x += dpp_mov<kDppBcast31, 0xC>(x);
-    return x;
-}
-
 // Automatic splits of a paged batch, from the lengths on the device (every
 // wave computes the same values).  The chunk: about kPagedTargetItems
 // workgroups for the whole batch, at least kPagedMinChunk keys, a multiple of
@@ -232,29 +141,6 @@ __device__ bool paged_auto_pair(const int *__restrict__ lens, int B, int cap, in
         acc += blk;
     }
     return false;
-}
-
-// Max over the lanes l and l^16 (resp. l^32): the four 16-lane groups of a
-// wave hold the same query heads for different keys.
-__device__ __forceinline__ float max_xor16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // (Two workgroups per CU as the register target: the kernel then fits in

@@ -39,9 +39,9 @@ __device__ __forceinline__ f32x16_t mma_f32(float a, float b, f32x16_t c)
 
 __device__ __forceinline__ unsigned wave_sum_u32(unsigned x)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+    // integer sum over the wave: any order gives the same result
+    const int i = wave_scan_i32((int)x);  // inclusive prefix sum, the total in lane 63
+    return (unsigned)__builtin_amdgcn_readlane(i, 63);
 }
 
 // Input elements widen exactly to fp32 on load (TI = float or __bf16, the
@@ -198,7 +198,7 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(mx);
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = fast_exp2((m_run - m_use) * scale_log2);
@@ -260,7 +260,7 @@ fwd_f32_kernel(const TI *__restrict__ Q, const TI *__restrict__ K,
                 }
     }
 
-    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l = sum_xor32(l_run);
     if (row < Nq) {
         const float den = PCAST ? p_scale * l : l;
         const float inv = l > 0.f ? 1.f / den : 0.f;

@@ -93,9 +93,12 @@ __device__ __forceinline__ void store_codes(uint8_t *__restrict__ codes, size_t 
 __device__ __forceinline__ float half_max(float v)
 {
     // maximum over the 32-lane half of the wave this lane belongs to
-#pragma unroll
-    for (int o = 1; o < 32; o *= 2) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    auto mx = [](float a, int b) { return fmaxf(a, __int_as_float(b)); };
+    v = mx(v, dpp_mov<kDppXor1>(__float_as_int(v)));
+    v = mx(v, dpp_mov<kDppXor2>(__float_as_int(v)));
+    v = mx(v, dpp_mov<kDppHalfMirror>(__float_as_int(v)));
+    v = mx(v, dpp_mov<kDppMirror>(__float_as_int(v)));
+    return max_xor16(v);
 }
 
 // Grid (ceil(nblk / 8), B*H); each wave covers two 32-row blocks.
@@ -163,7 +166,7 @@ quant_amax_kernel(const T *__restrict__ x, const float *__restrict__ signs, floa
 #pragma unroll
         for (int c = 0; c < D; ++c) m = fmaxf(m, fabsf(y[c]));
         m = half_max(m);
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = max_xor32(m);
         if (lane == 0) atomicMax(bits, __float_as_uint(m));
         return;
     }
@@ -173,7 +176,7 @@ quant_amax_kernel(const T *__restrict__ x, const float *__restrict__ signs, floa
     for (int c = 0; c < D; ++c) {
         float m = fabsf(y[c]);
         m = half_max(m);
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = max_xor32(m);
         if ((c & 63) == lane) mine[c / 64] = m;
     }
 #pragma unroll
