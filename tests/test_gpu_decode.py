@@ -238,6 +238,27 @@ def test_paged_full_length_equals_contiguous_and_clamps():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_paged_large_batch_streamed_equals_contiguous():
+    """A paged batch whose K and V exceed the streaming threshold (the
+    TinyLlama shape at full length: 134 MB) takes the non-temporal loads,
+    chosen on the device from the lengths, and automatic splits; it must give
+    the bits of fa_decode on the contiguous cache (also streamed, same
+    four-split partition)."""
+    need_gpu()
+    B, H, Hkv, d, ps, L = 16, 32, 4, 64, 128, 8192
+    assert 2 * B * Hkv * L * d * 2 >= 96 << 20
+    announce("fa_decode_paged, 134 MB batch (non-temporal loads) vs fa_decode")
+    q, k, v, kp, vp, table, _, _ = _paged_case(B, H, Hkv, [L] * B, ps, d, "bf16", seed=5)
+    dq = to_dev(q, "bf16")
+    o1, l1 = fa.decode(dq, to_dev(k, "bf16"), to_dev(v, "bf16"), scale=0.125)
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    o2, l2 = fa.decode_paged(dq, to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                             torch.from_numpy(table).cuda(), lens, scale=0.125)
+    torch.cuda.synchronize()
+    assert fa.decode_splits(B, H, Hkv, L) == 4
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_paged_ragged_poisoned_workspace_many_splits():
     """Splits past a sequence's end write nothing and the merge must not read
     them: the whole workspace starts as NaN, lengths are ragged (one empty),
