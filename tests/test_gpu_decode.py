@@ -238,6 +238,31 @@ def test_paged_full_length_equals_contiguous_and_clamps():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B", [129, 256])
+def test_paged_auto_many_sequences(B):
+    """Automatic splits over more than two 64-lane blocks of sequences: the
+    device-side length scan (sum and prefix sum across the blocks) must give
+    every (sequence, split) pair exactly once; seeded lengths with some
+    empty sequences, 64-key pages."""
+    need_gpu()
+    H, Hkv, d, dt, ps = 8, 2, 64, "bf16", 64
+    rng = np.random.default_rng(B)
+    lens = [0 if rng.random() < 0.1 else int(rng.integers(1, 400)) for _ in range(B)]
+    announce(f"fa_decode_paged automatic splits, B={B}")
+    q, k, v, kp, vp, table, _, _ = _paged_case(B, H, Hkv, lens, ps, d, dt, seed=B)
+    o, lse = fa.decode_paged(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt),
+                             torch.from_numpy(table).cuda(),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), scale=0.125)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
+            continue
+        o_ref, l_ref = oracle.attention(widen(q[b:b + 1], dt), widen(k[b:b + 1, :, :L], dt),
+                                        widen(v[b:b + 1, :, :L], dt), False, 0.125)
+        compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, dt, f"paged B={B} b={b} L={L}")
+
+
 def test_paged_large_batch_streamed_equals_contiguous():
     """A paged batch whose K and V exceed the streaming threshold (the
     TinyLlama shape at full length: 134 MB) takes the non-temporal loads,
