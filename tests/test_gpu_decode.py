@@ -386,3 +386,39 @@ def test_paged_large_batch_uses_uniform_split():
         o_ref, l_ref = oracle.attention(widen(q[b:b + 1], "bf16"), widen(k[b:b + 1, :, :L], "bf16"),
                                         widen(v[b:b + 1, :, :L], "bf16"), False, 0.125)
         compare(o[b:b + 1], lse[b:b + 1], o_ref, l_ref, "bf16", f"paged B=260 b={b} L={L}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 0])
+@pytest.mark.parametrize("pattern", ["growing", "falling"])
+def test_moving_max_every_step(pattern, splits, d):
+    """Scores that rise (or fall) steadily along the cache: with growing
+    keys every 128-key step raises each row's running max, so the rescale
+    of the accumulator runs at every step; with falling keys the first step
+    holds the max and later exponentials underflow.  One split (one
+    workgroup sweeps the whole cache) and the automatic split.  Outputs of
+    peaked rows are as large as the largest |v|, so the check is the
+    arithmetic bound u(|O| + max|v|) + 1e-3 (u = 2^-8 for bf16: P and O
+    rounded to bf16), and LSE within 1e-3."""
+    need_gpu()
+    B, H, Hkv, Nk, dt = 2, 16, 4, 3000, "bf16"
+    announce(f"fa_decode moving max ({pattern}) B={B} H={H}/{Hkv} Nk={Nk} d={d} splits={splits}")
+    nq = fagen.normal(fagen.stream_key(11, 81), B * H * d).reshape(B, H, 1, d)
+    nk = fagen.normal(fagen.stream_key(11, 82), B * Hkv * Nk * d).reshape(B, Hkv, Nk, d)
+    nv = fagen.normal(fagen.stream_key(11, 83), B * Hkv * Nk * d).reshape(B, Hkv, Nk, d)
+    j = np.arange(Nk, dtype=np.float64)
+    g = 1.0 + (j if pattern == "growing" else Nk - 1 - j) / 128.0
+    q = fagen.to_storage(1.0 + 0.25 * nq, dt)
+    k = fagen.to_storage(g[None, None, :, None] * (1.0 + 0.25 * nk), dt)
+    v = fagen.to_storage(nv, dt)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = fa.decode(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(widen(q, dt), widen(k, dt), widen(v, dt), False, scale)
+    # peaked rows: the bound of the prefill's peaked-row test (u = 2^-8)
+    og = o.float().cpu().numpy().astype(np.float64)
+    vmax = np.repeat(np.abs(widen(v, dt)).max(axis=(2, 3)), H // Hkv, axis=1)[:, :, None, None]
+    err = np.abs(og - o_ref)
+    assert np.all(err <= 2.0 ** -8 * (np.abs(o_ref) + vmax) + 1e-3), float(err.max())
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert float(np.abs(lg - lse_ref).max()) <= 1e-3

@@ -15,7 +15,7 @@ import torch
 import exact_io_aware_08_amd as fa
 import fagen
 import oracle
-from gpu_util import TORCH_DT, announce, compare, need_gpu, to_dev, widen
+from gpu_util import TOL, TORCH_DT, announce, compare, need_gpu, to_dev, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -221,3 +221,127 @@ def test_caller_outputs_are_checked():
     kv = torch.randn(2, 2, 300, 64, device="cuda").to(torch.bfloat16)
     with pytest.raises(ValueError):
         fa.decode(qd, kv, kv, out=torch.empty(2, 8, 64, device="cuda", dtype=torch.bfloat16))
+
+
+def _moving_max_inputs(B, H, Hkv, N, d, dt, pattern, seed):
+    """Q, K, V storage arrays whose scores move far across the key axis.
+
+    growing: q_i = 1 + noise, k_j = g(j)(1 + noise) with g(j) = 1 + j/64, so
+      at d = 64 a row's scores rise by about 1 (raw) per key, 4 nats per
+      32-key tile at scale 1/8: its exponentials leave any fixed
+      reference's 2^64 range within about a dozen tiles (and pass the fp16
+      maximum within three), while the scores stay small enough (a few
+      thousand) for fp32 accumulation to keep them to about 1e-3;
+    falling: the same with g reversed, so the first keys hold every row's
+      maximum and later exponentials underflow;
+    spike: iid keys, plus one key at N/2 aligned with every query (score
+      about 768 raw against order-1 scores elsewhere).
+    Values stay in the normal range of bf16 and fp16; the noise is the
+    seeded normal stream."""
+    nq = fagen.normal(fagen.stream_key(seed, 71), B * H * N * d).reshape(B, H, N, d)
+    nk = fagen.normal(fagen.stream_key(seed, 72), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    nv = fagen.normal(fagen.stream_key(seed, 73), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    j = np.arange(N, dtype=np.float64)
+    q = 1.0 + 0.25 * nq
+    if pattern == "growing":
+        k = (1.0 + j / 64.0)[None, None, :, None] * (1.0 + 0.25 * nk)
+    elif pattern == "falling":
+        k = (1.0 + (N - 1 - j) / 64.0)[None, None, :, None] * (1.0 + 0.25 * nk)
+    elif pattern == "spike":
+        k = 0.25 * nk
+        k[:, :, N // 2, :] = 12.0
+    else:
+        raise ValueError(pattern)
+    return (fagen.to_storage(q, dt), fagen.to_storage(k, dt), fagen.to_storage(nv, dt))
+
+
+def _check_peaked(o, lse, o_ref, lse_ref, v, dt, what):
+    """Peaked rows have outputs as large as the largest |v| (about 5 for
+    these inputs), where the stored 16-bit output alone is off by up to
+    u|O| (unit roundoff u = 2^-8 for bf16, 2^-11 for fp16), beyond the
+    2e-2 absolute bound sized for averaged outputs.  The bound used here
+    follows the arithmetic: P rounded to the input type before P V adds at
+    most u max|v| (the weights are normalised by the unrounded sum), the
+    output rounding u|O|, and 1e-3 covers the fp32 scores (about 1e-3 raw
+    at a few thousand), exp2 and accumulation.  The mean-abs and LSE bounds
+    are the usual ones."""
+    u = 2.0 ** -8 if dt == "bf16" else 2.0 ** -11
+    og = o.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(og)), what
+    B, H = og.shape[:2]
+    vw = np.abs(widen(v, dt)).max(axis=(2, 3))                 # [B, Hkv]
+    vmax = np.repeat(vw, H // vw.shape[1], axis=1)[:, :, None, None]
+    err = np.abs(og - o_ref)
+    bound = u * (np.abs(o_ref) + vmax) + 1e-3
+    worst = float((err / bound).max())
+    assert worst <= 1.0, (what, worst, float(err.max()))
+    assert float(err.mean()) <= TOL[dt]["mean_abs"], (what, float(err.mean()))
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lg), fin), what
+    lse_err = float(np.abs(lg[fin] - lse_ref[fin]).max())
+    assert lse_err <= TOL[dt]["lse"], (what, lse_err)
+    return dict(max_abs=float(err.max()), worst_over_bound=worst, lse=lse_err)
+
+
+def _reference_moves(q, k, dt, row, tile, scale):
+    """How often the kernel's lazy reference max must move for one causal
+    row of head 0 (a host-side restatement of its rule, to show that these
+    inputs reach that path): the reference starts as the first tile's max
+    and moves to a tile's max when that tile's exponentials, taken against
+    it, sum to 2^64 or more.  (With fp16 inputs the kernel also moves it
+    when a converted probability overflows, so this count is a lower
+    bound there.)"""
+    qf = widen(q, dt)[0, 0, row].astype(np.float64)
+    kf = widen(k, dt)[0, 0, : row + 1].astype(np.float64)
+    s = kf @ qf
+    c = scale * math.log2(math.e)
+    ref, moves = s[:tile].max(), 0
+    for t0 in range(tile, len(s), tile):
+        st = s[t0:t0 + tile]
+        with np.errstate(over="ignore"):
+            if np.exp2((st - ref) * c).sum() >= 2.0 ** 64:
+                ref, moves = max(ref, st.max()), moves + 1
+    return moves
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("pattern", ["growing", "spike"])
+def test_moving_max_large_grid_all_rows(dt, pattern):
+    """The 256-row instance (B=8, H=16, Hkv=4, N=2000: 1,024 workgroups of
+    256 rows), causal, with scores that force the reference max to move
+    during the sweep (the out-of-range rebase and its redone tile; for fp16
+    also the overflow of a converted probability); every row of every
+    head against the oracle, to the bound of _check_peaked."""
+    need_gpu()
+    B, H, Hkv, N, d = 8, 16, 4, 2000, 64
+    assert -(-N // 256) * B * H == 1024
+    announce(f"fa_fwd moving max ({pattern}) B={B} H={H}/{Hkv} N={N} {dt} causal")
+    q, k, v = _moving_max_inputs(B, H, Hkv, N, d, dt, pattern, seed=5)
+    assert fa.kv_tile(TORCH_DT[dt], d) == 32
+    assert _reference_moves(q, k, dt, N - 1, 32, 0.125) >= (3 if pattern == "growing" else 1)
+    o, lse = fa.fwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(widen(q, dt), widen(k, dt), widen(v, dt), True, 0.125)
+    m = _check_peaked(o, lse, o_ref, lse_ref, v, dt, f"moving max {pattern}")
+    announce(f"  {m}")
+
+
+@pytest.mark.parametrize("pattern", ["growing", "falling", "spike"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_moving_max_small_shapes_all_rows(pattern, causal, d):
+    """The same score patterns on the 128-row instance (d = 64), the
+    32-key-tile instance (d = 128) and the split-d instance (d = 256),
+    bf16, full and causal, every row, to the bound of _check_peaked."""
+    need_gpu()
+    B, H, Hkv, N = 1, 4, 2, 1000
+    dt = "bf16"
+    announce(f"fa_fwd moving max ({pattern}) B={B} H={H}/{Hkv} N={N} d={d} causal={causal}")
+    q, k, v = _moving_max_inputs(B, H, Hkv, N, d, dt, pattern, seed=6 + d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = fa.fwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(widen(q, dt), widen(k, dt), widen(v, dt), causal, scale)
+    m = _check_peaked(o, lse, o_ref, lse_ref, v, dt, f"moving max {pattern} d={d}")
+    announce(f"  {m}")
