@@ -1,4 +1,5 @@
-// fa_decode.hip -- split-KV decode with a fused log-sum-exp merge, gfx950.
+// fa_decode.hip -- split-KV decode with a log-sum-exp merge of the splits,
+// gfx950.
 //
 // One new query token per (batch, head) attends to a KV cache of Nk keys.
 // The key axis is cut into `splits` slices; each workgroup runs the online
@@ -9,11 +10,13 @@
 // merging the partials of any key partition with
 //   LSE = M + ln sum_s e^(lse_s - M),  O = sum_s e^(lse_s - LSE) O_s
 // gives the same result as one sweep.  A second, small kernel merges: one
-// wave per (batch, head) loads its partials in wide batches.  (A
-// merge inside the sweep kernel would need device-scope release/acquire
-// fences per workgroup, which on this chip write back and invalidate the
-// whole L2 of each XCD; the kernel boundary is far cheaper.)  With one split
-// the sweep kernel writes O and LSE itself.
+// wave per (batch, head) loads its partials in wide batches.  (A merge
+// inside the sweep kernel, by the last workgroup of each group to finish,
+// costs more than the kernel boundary on this chip: with device-scope
+// release/acquire fences, which write back and invalidate each XCD's whole
+// L2, or with device-scope relaxed stores and loads and an arrival ticket,
+// whose three dependent round trips to memory outlast a launch.)  With one
+// split the sweep kernel writes O and LSE itself.
 //
 // GQA: a workgroup serves up to 16 query heads that share one KV head, so
 // the KV slice is read once for all of them (gist.science "FlashAttention
