@@ -357,31 +357,34 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
 
     const TM mp(tid, (int)sizeof(T));
     const int tr_off = (4 * hh + ((lane & 15) >> 2)) * ST + 16 * (c >> 4) + 4 * (lane & 3);
-    u32x4_t qreg[TM::CH], greg[TM::CH];
-    float lreg = 0.f;  // threads 0..31: LSE of row tid; 32..63: D of row tid-32
-    // Global -> registers for the next iteration in order (it stays at the
-    // last iteration once reached).  The LSE is kept raw here and converted
-    // when staged: using it at once would make the wave wait for these loads
-    // in the same step.
+    u32x4_t qreg[2][TM::CH], greg[2][TM::CH];
+    float lreg[2] = {0.f, 0.f};  // threads 0..31: LSE of row tid; 32..63: D of row tid-32
+    // Global -> registers, iterations in order (it stays at the last
+    // iteration once reached), into two register sets: iteration i goes to
+    // set i & 1 two steps before it is staged, so each load has two steps to
+    // arrive (with one set, one step: 2% slower on the trading day,
+    // bit-identical).  The LSE is kept raw here and converted when staged:
+    // using it at once would make the wave wait for these loads in the same
+    // step.
     ItPos fp{0, 0, qt0};
-    auto fetch = [&]() {
+    auto fetch = [&](int rs) {
         const int hq = hk * G + fp.h, q0 = fp.qt * TK;
         const size_t qoff = ((size_t)b * H + hq) * Nq * D;
-        load_tile<D>(rows_rsrc<T, D>(Q + qoff, Nq, q0), mp, qreg);
-        load_tile<D>(rows_rsrc<T, D>(dO + qoff, Nq, q0), mp, greg);
+        load_tile<D>(rows_rsrc<T, D>(Q + qoff, Nq, q0), mp, qreg[rs]);
+        load_tile<D>(rows_rsrc<T, D>(dO + qoff, Nq, q0), mp, greg[rs]);
         if (tid < 2 * TK) {
             const int r = q0 + (tid & (TK - 1));
             const size_t ro = ((size_t)b * H + hq) * Nq + r;
-            lreg = 0.f;
-            if (r < Nq) lreg = tid < TK ? LSE[ro] : Dv[ro];
+            lreg[rs] = 0.f;
+            if (r < Nq) lreg[rs] = tid < TK ? LSE[ro] : Dv[ro];
         }
         if (fp.it < n_it - 1) advance(fp);
     };
-    auto stage = [&](int buf) {
-        store_tile<T, D>(Qbuf[buf], mp, qreg);
-        store_tile<T, D>(Gbuf[buf], mp, greg);
-        if (tid < TK) Lbuf[buf][tid] = lreg == -INFINITY ? 0.f : lreg * kLog2e;
-        else if (tid < 2 * TK) Dbuf[buf][tid - TK] = lreg;
+    auto stage = [&](int buf, int rs) {
+        store_tile<T, D>(Qbuf[buf], mp, qreg[rs]);
+        store_tile<T, D>(Gbuf[buf], mp, greg[rs]);
+        if (tid < TK) Lbuf[buf][tid] = lreg[rs] == -INFINITY ? 0.f : lreg[rs] * kLog2e;
+        else if (tid < 2 * TK) Dbuf[buf][tid - TK] = lreg[rs];
     };
 
     // Software pipeline over the iterations, as in the forward: step `it`
@@ -392,11 +395,12 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     // buffer 3 stands for iteration -1, whose operands are zero, and holds
     // zeros so that its products stay finite.
     if (n_it > 0) {
-        fetch();  // iteration 0
-        stage(0);
-        fetch();  // 1
-        stage(1);
-        fetch();  // 2
+        fetch(0);  // iteration 0
+        stage(0, 0);
+        fetch(0);  // 1
+        stage(1, 0);
+        fetch(0);  // 2, register set 0
+        fetch(1);  // 3, register set 1
         for (int i = tid; i < TK * ST / 8; i += 256) {
             reinterpret_cast<u32x4_t *>(Qbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
             reinterpret_cast<u32x4_t *>(Gbuf[3])[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -487,12 +491,12 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     if (n_it > 0) sdp(0, s_a, dp_a);
 
     // One step.  On entry: (sc, dpc) = S, dP of iteration it; (pp, dsp) =
-    // operands of iteration it-1; buffers (it-1..it+1) % 4 staged; the
-    // registers hold iteration it+2.
-    auto step = [&](int it, f32x16_t &sc, f32x16_t &dpc, f32x16_t &sn, f32x16_t &dpn,
+    // operands of iteration it-1; buffers (it-1..it+1) % 4 staged; register
+    // set it & 1 holds iteration it+2 and the other set iteration it+3.
+    auto step = [&](int it, int rs, f32x16_t &sc, f32x16_t &dpc, f32x16_t &sn, f32x16_t &dpn,
                     const v8 (&pp)[2], const v8 (&dsp)[2], v8 (&pc)[2], v8 (&dsc)[2]) {
-        stage((it + 2) & 3);  // last read (iteration it-2's dV/dK) before the previous barrier
-        fetch();              // iteration it+3
+        stage((it + 2) & 3, rs);  // last read (iteration it-2's dV/dK) before the previous barrier
+        fetch(rs);                // iteration it+4 into the set just staged (rs = it & 1)
         sdp((it + 1) & 3, sn, dpn);
         dkdv((it + 3) & 3, pp, dsp);  // iteration it-1
         pds(it, sc, dpc, pc, dsc);
@@ -500,11 +504,11 @@ bwd_dkdv_kernel(const T *__restrict__ Q, const T *__restrict__ K, const T *__res
     };
     int it = 0;
     for (; it + 1 < n_it; it += 2) {
-        step(it, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
-        step(it + 1, s_b, dp_b, s_a, dp_a, p_b, ds_b, p_a, ds_a);
+        step(it, 0, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
+        step(it + 1, 1, s_b, dp_b, s_a, dp_a, p_b, ds_b, p_a, ds_a);
     }
     if (it < n_it) {
-        step(it, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
+        step(it, 0, s_a, dp_a, s_b, dp_b, p_a, ds_a, p_b, ds_b);
         dkdv(it & 3, p_b, ds_b);  // the last iteration's deferred products
     } else if (n_it > 0) {
         dkdv((n_it - 1) & 3, p_a, ds_a);
