@@ -257,3 +257,33 @@ def test_incoherent_processing_lowers_error():
     # without outliers the rotation neither helps nor hurts much
     e = _rmse_vs_exact(1, 4, 1024, 64, 0.0, 1.0)
     assert 0.9 < e["naive"] / e["rotated"] < 1.1, e
+
+
+@pytest.mark.parametrize("rev,rot", [(False, False), (True, False), (False, True)])
+def test_fp8_moving_max_matches_emulation(rev, rot):
+    """Keys whose scores rise along the key axis (k_j = (1 + j/64)(1 + noise),
+    q_i = 1 + noise, bf16 before quantisation): in forward order every tile
+    raises each row's running max, so the rescale of O runs on every tile;
+    in reverse order the first tile holds the max and later tiles' P
+    underflow in E4M3.  Against the oracle's emulation on the dequantised
+    operands, as in test_fp8_matches_emulation."""
+    need_gpu()
+    B, H, Hkv, N, d = 1, 4, 2, 700, 64
+    announce(f"fa_fwd_fp8 moving max rev={rev} rot={rot}")
+    nq = fagen.normal(fagen.stream_key(21, 91), B * H * N * d).reshape(B, H, N, d)
+    nk = fagen.normal(fagen.stream_key(21, 92), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    nv = fagen.normal(fagen.stream_key(21, 93), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    g = 1.0 + np.arange(N, dtype=np.float64) / 64.0
+    q = widen(fagen.to_storage(1.0 + 0.25 * nq, "bf16"), "bf16")
+    k = widen(fagen.to_storage(g[None, None, :, None] * (1.0 + 0.25 * nk), "bf16"), "bf16")
+    v = widen(fagen.to_storage(nv, "bf16"), "bf16")
+    sg = fagen.random_signs(21, d) if rot else None
+    qc, qs = oracle.quant_e4m3(q, sg, "rows32", False)
+    kc, ks = oracle.quant_e4m3(k, sg, "rows32", False)
+    vc, vs = oracle.quant_e4m3(v, None, "channels", False)
+    deq = (oracle.dequant_e4m3(qc, qs), oracle.dequant_e4m3(kc, ks),
+           oracle.dequant_e4m3(vc, vs, "channels"))
+    scale = np.float32(1.0 / math.sqrt(d))
+    sc = float(np.float32(scale / d)) if rot else float(scale)
+    o, lse = _gpu_fp8((qc, qs, kc, ks, vc, vs), True, sc, 256.0, rev)
+    _check_vs_emulation(o, lse, deq, True, sc, 256.0, rev, "fp8 moving max", bound_heads=(0, 3))
