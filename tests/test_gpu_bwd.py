@@ -50,13 +50,13 @@ def _bounds(q, k, v, dout, o_given, o_exact, causal, scale, ad, ref):
     return bq, bk, bv
 
 
-def run_bwd(B, H, Hkv, Nq, Nk, d, dt, causal, seed=0, gpu_forward=False):
+def run_bwd(B, H, Hkv, Nq, Nk, d, dt, causal, seed=0, gpu_forward=False, inputs=None):
     need_gpu()
     announce(f"fa_bwd B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dt} causal={causal} "
-             f"seed={seed} gpu_forward={gpu_forward}")
+             f"seed={seed} gpu_forward={gpu_forward}" + (" (given inputs)" if inputs else ""))
     scale = float(np.float32(1.0 / math.sqrt(d)))
     cfg = dict(B=B, H=H, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, dtype=dt, kind="iid")
-    qs, ks, vs = fagen.make_inputs(cfg, seed)
+    qs, ks, vs = fagen.make_inputs(cfg, seed) if inputs is None else inputs
     gs = _dout(B, H, Nq, d, dt, seed)
     q, k, v, gout = (widen(x, dt) for x in (qs, ks, vs, gs))
     o_ex, lse_ex = oracle.attention(q, k, v, causal, scale)
@@ -162,3 +162,26 @@ def test_determinism():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def _growing_keys(B, H, Hkv, N, d, dt, seed):
+    """q_i = 1 + noise, k_j = (1 + j/64)(1 + noise), v iid (storage arrays):
+    scores rise along the key axis, so each row's softmax is peaked on its
+    last visible keys and the recomputed P spans many orders of magnitude."""
+    nq = fagen.normal(fagen.stream_key(seed, 61), B * H * N * d).reshape(B, H, N, d)
+    nk = fagen.normal(fagen.stream_key(seed, 62), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    nv = fagen.normal(fagen.stream_key(seed, 63), B * Hkv * N * d).reshape(B, Hkv, N, d)
+    g = 1.0 + np.arange(N, dtype=np.float64) / 64.0
+    return (fagen.to_storage(1.0 + 0.25 * nq, dt),
+            fagen.to_storage(g[None, None, :, None] * (1.0 + 0.25 * nk), dt),
+            fagen.to_storage(nv, dt))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_growing_scores(causal, d):
+    """Peaked rows (scores rising along the key axis) through the same
+    bound as the other cases."""
+    B, H, Hkv, N = 1, 4, 2, 600
+    run_bwd(B, H, Hkv, N, N, d, "bf16", causal, seed=d,
+            inputs=_growing_keys(B, H, Hkv, N, d, "bf16", seed=d))
